@@ -1,0 +1,191 @@
+"""Benchmark of the attention forward pass on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = one full forward pass (fa_fwd) over the workload's tensors, which
+are drawn (seeded) and uploaded to HBM before timing starts.  Prints ONE JSON
+line on stdout.  Default workload: causal bf16, B=1, H_q=32, H_kv=8,
+qL=kL=8192, D=128.
+
+  value     algorithmic TFLOP/s of the timed steps (4*B*H_q*qL*kL*D, halved
+            for causal), wall clock between two device synchronisations
+  roofline  the kernel's achieved TFLOP/s from HIP events recorded around
+            each launch on the launch stream, against the MI355X dense matrix
+            peak for the dtype
+  cpu_baseline  the fp64 CPU oracle, timed on this host on a bounded sample
+            of the same workload's query rows
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X dense matrix peaks (TFLOP/s) and HBM bandwidth (GB/s), published
+# figures: 256 CUs at 2.4 GHz.
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w) -> int:
+    esz = 2 if w.dtype == "bf16" else 4
+    qo = 2 * w.B * w.Hq * w.qL * w.D * esz
+    kv = 2 * w.B * w.Hkv * w.kL * w.D * esz
+    lse = w.B * w.Hq * w.qL * 4
+    mask = 0
+    if w.mask_kind == "additive":
+        mask = w.B * w.Hq * w.qL * w.kL * esz
+    elif w.mask_kind == "bool":
+        mask = w.B * w.Hq * w.qL * w.kL
+    return qo + kv + lse + mask
+
+
+def cpu_baseline(w, q, k, v, mask, target_s: float):
+    """Time the fp64 oracle on a uniform random sample of query rows.
+
+    Row counts are calibrated so the timed run is about target_s seconds.
+    FLOP per row = 4*D*(number of keys the row attends under the causal rule),
+    the same accounting as the GPU metric.
+    """
+    import numpy as np
+
+    from oracle import OracleLib
+
+    lib = OracleLib()
+    qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    md, kind = None, "none"
+    if mask is not None:
+        kind = "bool" if w.mask_kind == "bool" else "additive"
+        md = mask.double().numpy() if kind == "additive" else mask.numpy()
+    total_rows = w.B * w.Hq * w.qL
+    rng = np.random.default_rng(99)
+
+    def run(n):
+        rows = np.sort(rng.choice(total_rows, size=min(n, total_rows), replace=False)).astype(np.int64)
+        i = rows % w.qL
+        keys = np.minimum(i + 1, w.kL) if w.causal else np.full(rows.shape, w.kL)
+        flops = float(4.0 * w.D * keys.sum())
+        t0 = time.perf_counter()
+        lib.fwd(qd, kd, vd, scale=w.scale, causal=w.causal, mask=md, mask_kind=kind, rows=rows)
+        return time.perf_counter() - t0, flops, rows.size
+
+    dt, _, n = run(256)
+    n2 = int(min(total_rows, max(256, 256 * target_s / max(dt, 1e-3))))
+    dt, flops, n = run(n2)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": lib.threads(), "kind": "oracle",
+            "sample": f"{n} query rows drawn uniformly from the {total_rows} rows of {w.name} "
+                      f"(fp64, {dt:.1f} s, {flops / 1e9:.1f} GFLOP)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="causal_bf16_d128_8k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              f"(the attention path needs no cross-GPU exchange; see the sharding notes in the docs).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import flashattention_forward_04_amd as fa
+    import workloads as W
+
+    w = W.CONFIGS.get(args.workload) or {x.name: x for x in W.RAGGED}[args.workload]
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
+    log(f"workload: {w.name}: {w.note}")
+
+    q, k, v, mask = W.draw(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    md = None if mask is None else mask.to(dev)
+    out = None
+    if w.token_major_out:
+        out = torch.empty((w.B, w.qL, w.Hq, w.D), dtype=q.dtype, device=dev).transpose(1, 2)
+    else:
+        out = torch.empty((w.B, w.Hq, w.qL, w.D), dtype=q.dtype, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.qL), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.fwd(qd, kd, vd, mask=md, causal=w.causal, scale=w.scale, out=out, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-launch kernel durations from HIP events on the launch stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    ms_per_step = wall * 1e3 / args.steps
+
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kern_avg_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    log(f"kernel avg {kern_avg_ms * 1e3:.1f} us (min {min(kern_ms) * 1e3:.1f}, max {max(kern_ms) * 1e3:.1f}); "
+        f"{achieved:.1f} TFLOP/s = {100 * achieved / peak:.1f}% of {peak} TFLOP/s")
+    nbytes = algorithmic_bytes(w)
+    log(f"algorithmic bytes {nbytes / 1e6:.1f} MB -> {nbytes / (kern_avg_ms * 1e-3) / 1e9:.0f} GB/s "
+        f"({100 * nbytes / (kern_avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS:.1f}% of HBM)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, q, k, v, mask, args.cpu_seconds)
+        log(f"cpu baseline: {cpu}")
+
+    res = {
+        "metric": "attention fwd TFLOP/s + % MFMA peak, bf16 D=128 causal qL=kL=8192",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V)",
+        "config": {"workload": w.name, "B": w.B, "H_q": w.Hq, "H_kv": w.Hkv, "qL": w.qL, "kL": w.kL, "D": w.D,
+                   "causal": w.causal, "mask": w.mask_kind, "scale": w.scale,
+                   "o_layout": "token-major" if w.token_major_out else "head-major",
+                   "flop_per_step": flops},
+        "mfma_peak_frac": round(achieved / peak, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel_avg_us": round(kern_avg_ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

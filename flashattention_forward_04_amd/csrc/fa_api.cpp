@@ -1,0 +1,200 @@
+// fa_api.cpp - the C ABI of libfa_mi355x: argument checks, variant selection
+// and launch on the caller's stream.  See include/fa_mi355x.h for the
+// contract of every entry point.
+//
+// The checks follow mlx-native flash_attn_train.rs (validate_params: every
+// size positive, H_q divisible by H_kv; dispatch_inner: head_dim and dtype
+// checks before any launch) and add this library's own pointer, alignment
+// and stride rules.  Everything is checked before anything is launched.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "fa_common.h"
+#include "fa_mi355x.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+fa_status fail(fa_status st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+const fa::Variant* find_variant(int dtype, int D, int mask, int causal)
+{
+    int n = 0;
+    const fa::Variant* tab = dtype == FA_DTYPE_BF16 ? fa::variants_bf16(&n) : fa::variants_f32(&n);
+    for (int i = 0; i < n; ++i)
+        if (tab[i].D == D && tab[i].mask == mask && tab[i].causal == (causal ? 1 : 0)) return &tab[i];
+    return nullptr;
+}
+
+bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+bool all_zero(const int64_t s[3]) { return s[0] == 0 && s[1] == 0 && s[2] == 0; }
+
+// Contiguous default {batch, head, seq} strides of a [B, H, L, inner] tensor.
+void default_strides(int64_t out[3], int64_t H, int64_t Lx, int64_t inner)
+{
+    out[2] = inner;
+    out[1] = Lx * inner;
+    out[0] = H * Lx * inner;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s)
+{
+    switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARGUMENT: return "FA_ERR_INVALID_ARGUMENT";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    }
+    return "FA_ERR_UNKNOWN";
+}
+
+const char* fa_last_error(void) { return g_last_error; }
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+int fa_variant_count(void)
+{
+    int nb = 0, nf = 0;
+    fa::variants_bf16(&nb);
+    fa::variants_f32(&nf);
+    return nb + nf;
+}
+
+const char* fa_variant_name(int i)
+{
+    int nb = 0, nf = 0;
+    const fa::Variant* tb = fa::variants_bf16(&nb);
+    const fa::Variant* tf = fa::variants_f32(&nf);
+    if (i < 0) return nullptr;
+    if (i < nb) return tb[i].name;
+    i -= nb;
+    if (i < nf) return tf[i].name;
+    return nullptr;
+}
+
+int fa_supported(fa_dtype dtype, int D, fa_mask_kind mask_kind, int causal)
+{
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return 0;
+    if (mask_kind < FA_MASK_NONE || mask_kind > FA_MASK_BOOL) return 0;
+    return find_variant(dtype, D, mask_kind, causal) != nullptr;
+}
+
+fa_status fa_fwd_strided(const void* Q, const void* K, const void* V, const void* mask,
+                         void* O, float* L,
+                         int B, int H_q, int H_kv, int qL, int kL, int D,
+                         float scale, int causal,
+                         fa_dtype dtype, fa_mask_kind mask_kind,
+                         const fa_strides* strides, void* hip_stream)
+{
+    g_last_error[0] = '\0';
+    const fa_status E = FA_ERR_INVALID_ARGUMENT;
+    if (B <= 0) return fail(E, "fa_fwd: B must be > 0, got %d", B);
+    if (H_q <= 0) return fail(E, "fa_fwd: H_q must be > 0, got %d", H_q);
+    if (H_kv <= 0) return fail(E, "fa_fwd: H_kv must be > 0, got %d", H_kv);
+    if (H_q % H_kv != 0) return fail(E, "fa_fwd: H_q (%d) must be divisible by H_kv (%d)", H_q, H_kv);
+    if (qL <= 0) return fail(E, "fa_fwd: qL must be > 0, got %d", qL);
+    if (kL <= 0) return fail(E, "fa_fwd: kL must be > 0, got %d", kL);
+    if (D != 64 && D != 128 && D != 256) return fail(E, "fa_fwd: D must be 64, 128 or 256, got %d", D);
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return fail(E, "fa_fwd: unknown dtype %d", (int)dtype);
+    if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_ADDITIVE && mask_kind != FA_MASK_BOOL)
+        return fail(E, "fa_fwd: unknown mask kind %d", (int)mask_kind);
+    if ((mask_kind == FA_MASK_NONE) != (mask == nullptr))
+        return fail(E, "fa_fwd: mask must be NULL exactly when mask_kind is FA_MASK_NONE");
+    if (!Q || !K || !V || !O || !L) return fail(E, "fa_fwd: Q, K, V, O and L must be non-NULL");
+    if (!std::isfinite(scale)) return fail(E, "fa_fwd: scale must be finite");
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(L, 4))
+        return fail(E, "fa_fwd: Q, K, V and O must be 16-byte aligned and L 4-byte aligned");
+    if ((int64_t)B * H_q * qL * D > INT64_MAX / 8 || (int64_t)B * H_q * qL * kL > INT64_MAX / 8)
+        return fail(E, "fa_fwd: tensor too large");
+
+    const int esz = dtype == FA_DTYPE_BF16 ? 2 : 4;
+    const int vec_elems = 16 / esz;
+    fa::FwdParams p;
+    std::memset(&p, 0, sizeof(p));
+    fa_strides s;
+    if (strides) s = *strides;
+    else std::memset(&s, 0, sizeof(s));
+    if (all_zero(s.q)) default_strides(s.q, H_q, qL, D);
+    if (all_zero(s.k)) default_strides(s.k, H_kv, kL, D);
+    if (all_zero(s.v)) default_strides(s.v, H_kv, kL, D);
+    if (all_zero(s.o)) default_strides(s.o, H_q, qL, D);
+    if (all_zero(s.mask)) default_strides(s.mask, H_q, qL, kL);
+    const struct { const int64_t* st; const char* name; } t4[] = {{s.q, "Q"}, {s.k, "K"}, {s.v, "V"}, {s.o, "O"}};
+    for (const auto& t : t4)
+        for (int a = 0; a < 3; ++a)
+            if (t.st[a] < 0 || t.st[a] % vec_elems != 0)
+                return fail(E, "fa_fwd: %s stride %d (%lld) must be a non-negative multiple of %d elements",
+                            t.name, a, (long long)t.st[a], vec_elems);
+    for (int a = 0; a < 3; ++a)
+        if (s.mask[a] < 0) return fail(E, "fa_fwd: mask strides must be non-negative");
+
+    const fa::Variant* var = find_variant(dtype, D, mask_kind, causal);
+    if (!var)
+        return fail(FA_ERR_UNSUPPORTED, "fa_fwd: no kernel built for dtype %d, D %d, mask %d, causal %d",
+                    (int)dtype, D, (int)mask_kind, causal);
+
+    p.q = Q;
+    p.k = K;
+    p.v = V;
+    p.mask = mask;
+    p.o = O;
+    p.lse = L;
+    for (int a = 0; a < 3; ++a) {
+        p.q_s[a] = s.q[a];
+        p.k_s[a] = s.k[a];
+        p.v_s[a] = s.v[a];
+        p.o_s[a] = s.o[a];
+        p.m_s[a] = s.mask[a];
+    }
+    p.B = B;
+    p.Hq = H_q;
+    p.Hkv = H_kv;
+    p.qL = qL;
+    p.kL = kL;
+    p.group = H_q / H_kv;
+    p.n_qtiles = (qL + var->block_m - 1) / var->block_m;
+    p.neg_q = scale < 0.f ? 1 : 0;
+    p.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
+    if (mask_kind != FA_MASK_NONE) {
+        // 4 consecutive mask entries load as one vector when every row start is
+        // aligned to 4 elements' worth of bytes.
+        const int mesz = mask_kind == FA_MASK_BOOL ? 1 : esz;
+        const uintptr_t need = (uintptr_t)4 * mesz;
+        p.mask_vec = aligned(mask, need) && s.mask[0] % 4 == 0 && s.mask[1] % 4 == 0 && s.mask[2] % 4 == 0;
+    }
+    if ((int64_t)p.n_qtiles * H_q * B > 0x7fffffffLL) return fail(E, "fa_fwd: grid too large");
+
+    const hipError_t err = var->launch(p, (hipStream_t)hip_stream);
+    if (err != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd: launch of %s failed: %s", var->name, hipGetErrorString(err));
+    return FA_OK;
+}
+
+fa_status fa_fwd(const void* Q, const void* K, const void* V, const void* mask,
+                 void* O, float* L,
+                 int B, int H_q, int H_kv, int qL, int kL, int D,
+                 float scale, int causal,
+                 fa_dtype dtype, fa_mask_kind mask_kind, void* hip_stream)
+{
+    return fa_fwd_strided(Q, K, V, mask, O, L, B, H_q, H_kv, qL, kL, D, scale, causal, dtype, mask_kind,
+                          nullptr, hip_stream);
+}
+
+}  // extern "C"

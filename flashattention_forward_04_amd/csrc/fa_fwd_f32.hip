@@ -1,0 +1,291 @@
+// fa_fwd_f32.hip - FlashAttention-2 forward, fp32 in/out, for gfx950.
+//
+// Same algorithm as the bf16 kernel (mlx-native flash_attn_train.rs, module
+// doc "Algorithm"), with every operand kept in fp32: Q, K, V, the scores, P
+// and the accumulators.  The oxibonsai dit_attention_flash.rs module doc
+// reports that staging full-range values in half precision broke its 1e-3
+// parity bound, so this path never rounds P or the operands down.
+//
+// CDNA4 mapping:
+//   * Both products run on v_mfma_f32_32x32x2_f32.  As in the bf16 kernel the
+//     score tile is formed transposed, S^T = K Q^T, so lane l holds 16 keys
+//     of query row l%32 and row reductions stay in-lane plus one exchange
+//     with lane l^32; the output is accumulated as O^T = V^T P^T so the
+//     per-row rescale multiplies the lane's own registers.
+//   * The head dimension is contracted in an order that lets one 16-byte LDS
+//     read of K feed four MFMAs: step 4t+e uses element 8t + 4(l/32) + e.  Q
+//     is held in VGPRs in the matching order.
+//   * Score register r of S^T is the P operand of one O^T step directly
+//     (fp32 MFMAs take one k element per lane), and V^T is staged in LDS so
+//     one 16-byte read yields the V operand of four consecutive steps.
+//   * Output rows are written through the caller's strides, which is how the
+//     token-major [seq, heads*D] layout of the DiT joint attention
+//     (oxibonsai dit_attention_flash.rs, module doc) is produced in place.
+#include "fa_common.h"
+
+#include <math.h>
+
+namespace fa {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+template <int D, int MASK, bool CAUSAL, int NW, int BN>
+__global__ void __launch_bounds__(NW * 64)
+fwd_f32_kernel(const FwdParams p)
+{
+    constexpr int NT = NW * 64;
+    constexpr int BM = NW * 32;
+    constexpr int KP = D + 4;   // K row pitch in LDS (floats)
+    constexpr int VP = BN + 4;  // V^T row pitch in LDS (floats)
+    constexpr int DT = D / 8;   // groups of four k-steps over the head dimension
+    constexpr int NC = BN / 32;
+    constexpr int ND = D / 32;
+    static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+
+    __shared__ __attribute__((aligned(16))) float Ks[BN * KP];
+    __shared__ __attribute__((aligned(16))) float Vt[D * VP];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int r32 = lane & 31;
+    const int g = lane >> 5;
+
+    int id = blockIdx.x;
+    const int h = id % p.Hq;
+    id /= p.Hq;
+    const int b = id % p.B;
+    id /= p.B;
+    const int qt = CAUSAL ? (p.n_qtiles - 1 - id) : id;
+    const int q0 = qt * BM;
+    const int hk = h / p.group;
+    const int wq0 = q0 + wave * 32;
+    const int qrow = wq0 + r32;
+
+    const float* Qb = (const float*)p.q + b * p.q_s[0] + h * p.q_s[1];
+    const float* Kb = (const float*)p.k + b * p.k_s[0] + hk * p.k_s[1];
+    const float* Vb = (const float*)p.v + b * p.v_s[0] + hk * p.v_s[1];
+
+    // Q: qf[t] = Q[qrow][8t + 4g .. +3]
+    f32x4 qf[DT];
+    {
+        const bool in = qrow < p.qL;
+        const f32x4* src = (const f32x4*)(Qb + (int64_t)(in ? qrow : 0) * p.q_s[2]);
+        const float sgn = p.neg_q ? -1.f : 1.f;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) qf[t] = in ? src[2 * t + g] * sgn : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const float c2 = p.scale_log2;
+    const int kv_end = CAUSAL ? min(p.kL, min(p.qL, q0 + BM)) : p.kL;
+
+    const uint8_t* mrow = nullptr;
+    if (MASK != MASK_NONE) {
+        const int qc = min(qrow, p.qL - 1);
+        const int esz = (MASK == MASK_BOOL) ? 1 : 4;
+        mrow = (const uint8_t*)p.mask + (b * p.m_s[0] + h * p.m_s[1] + (int64_t)qc * p.m_s[2]) * esz;
+    }
+
+    f32x16 o[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) o[d] = f32x16{};
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+
+    for (int j0 = 0; j0 < kv_end; j0 += BN) {
+        __syncthreads();
+        // ---- stage K row-major ----
+        constexpr int KCH = BN * D / 4;
+#pragma unroll
+        for (int it = 0; it < (KCH + NT - 1) / NT; ++it) {
+            const int c = tid + it * NT;
+            if (KCH % NT != 0 && c >= KCH) break;
+            const int row = c / (D / 4);
+            const int col = c % (D / 4);
+            const int j = j0 + row;
+            f32x4 w = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (j < p.kL) w = *(const f32x4*)(Kb + (int64_t)j * p.k_s[2] + col * 4);
+            *(f32x4*)(Ks + row * KP + col * 4) = w;
+        }
+        // ---- stage V transposed: Vt[d][j], 4 keys x 4 dims per unit ----
+        constexpr int VU = (BN / 4) * (D / 4);
+#pragma unroll
+        for (int it = 0; it < (VU + NT - 1) / NT; ++it) {
+            const int u = tid + it * NT;
+            if (VU % NT != 0 && u >= VU) break;
+            const int w4 = u % (D / 4);
+            const int qd = u / (D / 4);
+            f32x4 r[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = j0 + 4 * qd + e;
+                r[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (j < p.kL) r[e] = *(const f32x4*)(Vb + (int64_t)j * p.v_s[2] + w4 * 4);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *(f32x4*)(Vt + (4 * w4 + i) * VP + 4 * qd) = f32x4{r[0][i], r[1][i], r[2][i], r[3][i]};
+        }
+        __syncthreads();
+
+        if (CAUSAL && j0 > wq0 + 31) continue;
+
+        // ---- S^T = K Q^T ----
+        f32x16 s[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) s[c] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const f32x4 kv = *(const f32x4*)(Ks + (32 * c + r32) * KP + 8 * t + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    s[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[e], qf[t][e], s[c], 0, 0, 0);
+            }
+        }
+
+        const bool fast = (MASK == MASK_NONE) && (j0 + BN <= p.kL) && (!CAUSAL || j0 + BN - 1 <= wq0);
+        float cs = c2;
+        if (!fast) {
+            cs = 1.f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int jb = j0 + 32 * c + 8 * rq + 4 * g;
+                    float mv[4] = {0.f, 0.f, 0.f, 0.f};
+                    bool mb[4] = {true, true, true, true};
+                    if (MASK == MASK_ADD) {
+                        if (p.mask_vec && jb + 3 < p.kL) {
+                            const f32x4 w = *(const f32x4*)(mrow + 4 * (int64_t)jb);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) mv[e] = w[e];
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (jb + e < p.kL) mv[e] = ((const float*)mrow)[jb + e];
+                        }
+                    } else if (MASK == MASK_BOOL) {
+                        if (p.mask_vec && jb + 3 < p.kL) {
+                            const uint32_t w = *(const uint32_t*)(mrow + jb);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) mb[e] = ((w >> (8 * e)) & 0xffu) != 0;
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) mb[e] = (jb + e < p.kL) ? (mrow[jb + e] != 0) : false;
+                        }
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = jb + e;
+                        bool ok = (j < p.kL) && mb[e];
+                        if (CAUSAL) ok = ok && (j <= qrow);
+                        float t = s[c][4 * rq + e] * c2;
+                        if (MASK == MASK_ADD) t = __builtin_fmaf(mv[e], kLog2e, t);
+                        s[c][4 * rq + e] = ok ? t : -INFINITY;
+                    }
+                }
+            }
+        }
+
+        float mx = s[0][0];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c][r]);
+        mx = fmaxf(mx, xor32(mx));
+        const float m_new = fmaxf(m_run, mx * cs);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
+        float rs = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][r], cs, -m_use));
+                s[c][r] = e;
+                rs += e;
+            }
+        rs += xor32(rs);
+        l_run = l_run * corr + rs;
+        m_run = m_new;
+#pragma unroll
+        for (int d = 0; d < ND; ++d) o[d] *= corr;
+
+        // ---- O^T += V^T P^T: step r of key block c is key 32c + 8(r/4) + 4g + r%4 ----
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+#pragma unroll
+                for (int d = 0; d < ND; ++d) {
+                    const f32x4 vv = *(const f32x4*)(Vt + (32 * d + r32) * VP + 32 * c + 8 * rq + 4 * g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        o[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[e], s[c][4 * rq + e], o[d], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    if (qrow < p.qL) {
+        const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
+        float* orow = (float*)p.o + b * p.o_s[0] + h * p.o_s[1] + (int64_t)qrow * p.o_s[2];
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const f32x4 w = f32x4{o[d][4 * rq + 0], o[d][4 * rq + 1], o[d][4 * rq + 2], o[d][4 * rq + 3]} * inv;
+                *(f32x4*)(orow + 32 * d + 8 * rq + 4 * g) = w;
+            }
+        if (g == 0) {
+            const float lse = (l_run > 0.f) ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : 0.f;
+            p.lse[((int64_t)b * p.Hq + h) * p.qL + qrow] = lse;
+        }
+    }
+}
+
+template <int D, int MASK, bool CAUSAL, int NW, int BN>
+hipError_t launch_f32(const FwdParams& p, hipStream_t st)
+{
+    const dim3 grid((unsigned)p.n_qtiles * p.Hq * p.B);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, MASK, CAUSAL, NW, BN>), grid, dim3(NW * 64), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+#define FA_F32_VARIANT(D, MASK, CAUSAL, NW, BN, NAME) \
+    {NAME, 0, D, MASK, CAUSAL, NW * 32, &launch_f32<D, MASK, CAUSAL, NW, BN>}
+
+#define FA_F32_FOR_D(D, NW, BN)                                                         \
+    FA_F32_VARIANT(D, MASK_NONE, false, NW, BN, "fwd_f32_d" #D "_nomask"),              \
+    FA_F32_VARIANT(D, MASK_NONE, true, NW, BN, "fwd_f32_d" #D "_nomask_causal"),        \
+    FA_F32_VARIANT(D, MASK_ADD, false, NW, BN, "fwd_f32_d" #D "_additive"),             \
+    FA_F32_VARIANT(D, MASK_ADD, true, NW, BN, "fwd_f32_d" #D "_additive_causal"),       \
+    FA_F32_VARIANT(D, MASK_BOOL, false, NW, BN, "fwd_f32_d" #D "_bool"),                \
+    FA_F32_VARIANT(D, MASK_BOOL, true, NW, BN, "fwd_f32_d" #D "_bool_causal")
+
+// Host-only accessor: a namespace-scope const table would also be emitted
+// for the device, where the launch functions do not exist.
+const Variant* variants_f32(int* n)
+{
+    static const Variant table[] = {
+    FA_F32_FOR_D(64, 4, 32),
+    FA_F32_FOR_D(128, 4, 32),
+    FA_F32_FOR_D(256, 4, 32),
+};
+    *n = (int)(sizeof(table) / sizeof(table[0]));
+    return table;
+}
+
+}  // namespace fa

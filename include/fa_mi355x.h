@@ -1,0 +1,139 @@
+/*
+ * fa_mi355x.h - C ABI of libfa_mi355x, a FlashAttention-2 forward pass for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (mlx-native flash_attn_train.rs, module doc "Algorithm" and
+ * "Buffer layout"; oxibonsai dit_attention_flash.rs, module doc "Flash-attention
+ * v2 structure"; ruDNN dense_attention.rs, `forward`):
+ *
+ *   for batch b, query head h, query row i, kv head g = h / (H_q / H_kv):
+ *     s_ij   = scale * sum_d Q[b,h,i,d] K[b,g,j,d]   (+ mask[b,h,i,j], additive)
+ *     key j is allowed iff j <= i when causal (top-left: row i sees keys
+ *     0..i, whatever qL and kL are), the bool mask entry is nonzero, and
+ *     s_ij != -inf
+ *     O[b,h,i,:] = sum_j softmax_j(s_ij) V[b,g,j,:]   over the allowed keys
+ *     L[b,h,i]   = ln sum_j exp(s_ij)                 (natural log)
+ *   A row with no allowed key gets O = 0 and L = 0 (forge
+ *   flash_attention_mma.metal, epilogue of flash_attn_fwd_mma).
+ *
+ * `scale` is the natural-domain factor, typically 1/sqrt(D); the library
+ * folds log2(e) in itself (mlx-native flash_attn_train.rs, module doc "Scale
+ * convention").  The additive mask is added after scaling (ruDNN `forward`).
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer is a DEVICE pointer on the current HIP device; the caller
+ *     owns all of them.  Q, K, V and the mask are read-only; O and L are
+ *     overwritten in full (rows beyond qL and padding are never touched).
+ *   - The call enqueues work on `hip_stream` (a hipStream_t; NULL = the null
+ *     stream) and returns without synchronising.  The forward pass allocates
+ *     no device memory.
+ *   - All argument checks run before any launch: a failed check writes
+ *     nothing, launches nothing and returns FA_ERR_INVALID_ARGUMENT (or
+ *     FA_ERR_UNSUPPORTED for a valid combination that is not built), with a
+ *     message in fa_last_error().  A failed launch returns FA_ERR_HIP.
+ *   - Buffer sizes cannot be checked through raw pointers; the Python binding
+ *     checks them (cf. mlx-native flash_attn_train.rs, validate_buffer_size).
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARGUMENT = 1, /* a check below failed; nothing was launched */
+    FA_ERR_UNSUPPORTED = 2,      /* valid but not built (e.g. an unbuilt head_dim) */
+    FA_ERR_HIP = 3               /* the HIP runtime reported an error at launch */
+} fa_status;
+
+typedef enum {
+    FA_DTYPE_F32 = 0, /* Q, K, V, O fp32; fp32 matrix products, P kept in fp32 */
+    FA_DTYPE_BF16 = 1 /* Q, K, V, O bf16; fp32 accumulation, P rounded to bf16 */
+} fa_dtype;
+
+typedef enum {
+    FA_MASK_NONE = 0,
+    FA_MASK_ADDITIVE = 1, /* same dtype as Q; added to the scaled score; -inf excludes */
+    FA_MASK_BOOL = 2      /* uint8; nonzero = attend (ruDNN `forward`, mask_kind 1) */
+} fa_mask_kind;
+
+/*
+ * fa_fwd - the forward pass on contiguous head-major tensors.
+ *
+ *   Q    [B, H_q,  qL, D]   dtype            (read)
+ *   K    [B, H_kv, kL, D]   dtype            (read)
+ *   V    [B, H_kv, kL, D]   dtype            (read)
+ *   mask [B, H_q,  qL, kL]  see fa_mask_kind (read; NULL iff FA_MASK_NONE)
+ *   O    [B, H_q,  qL, D]   dtype            (written)
+ *   L    [B, H_q,  qL]      fp32             (written)
+ *
+ * Checks (mlx-native flash_attn_train.rs, validate_params, plus this
+ * library's own): B, H_q, H_kv, qL, kL > 0; H_q % H_kv == 0; D in
+ * {64, 128, 256}; known dtype and mask kind; mask non-NULL iff a mask kind
+ * is given; Q, K, V, O, L non-NULL and 16-byte aligned; scale finite;
+ * element counts fit in int64.
+ */
+fa_status fa_fwd(const void* Q, const void* K, const void* V, const void* mask,
+                 void* O, float* L,
+                 int B, int H_q, int H_kv, int qL, int kL, int D,
+                 float scale, int causal,
+                 fa_dtype dtype, fa_mask_kind mask_kind, void* hip_stream);
+
+/*
+ * Element strides {batch, head, seq} of each tensor; the D axis (the kL axis
+ * for the mask) is always contiguous.  An all-zero triple selects the
+ * contiguous head-major default shown for fa_fwd.  A mask stride of 0 on a
+ * non-default triple broadcasts that axis (ruDNN dense_attention.rs,
+ * mask_offset).  Token-major O ([qL, H_q*D] per batch, the oxibonsai
+ * dit_attention_flash.rs output layout) is o = {qL*H_q*D, D, H_q*D}.
+ * Q, K, V and O strides must be non-negative multiples of 16 bytes' worth of
+ * elements (8 for bf16, 4 for fp32) so rows stay 16-byte aligned; mask
+ * strides may be any non-negative value.
+ */
+typedef struct {
+    int64_t q[3];
+    int64_t k[3];
+    int64_t v[3];
+    int64_t o[3];
+    int64_t mask[3];
+} fa_strides;
+
+/* fa_fwd with explicit strides (NULL = all defaults).  Same checks, plus the
+ * stride rules above; L is always contiguous [B, H_q, qL]. */
+fa_status fa_fwd_strided(const void* Q, const void* K, const void* V, const void* mask,
+                         void* O, float* L,
+                         int B, int H_q, int H_kv, int qL, int kL, int D,
+                         float scale, int causal,
+                         fa_dtype dtype, fa_mask_kind mask_kind,
+                         const fa_strides* strides, void* hip_stream);
+
+/* 1 if (dtype, D, mask_kind, causal) has a compiled kernel, else 0. */
+int fa_supported(fa_dtype dtype, int D, fa_mask_kind mask_kind, int causal);
+
+/* Number of compiled kernel variants, and the name of variant i (NULL past
+ * the end); the names are static strings (cf. the kernel-name lists that
+ * mlx-native flash_attn_train.rs exposes to its tests). */
+int fa_variant_count(void);
+const char* fa_variant_name(int i);
+
+/* Static text for a status code. */
+const char* fa_status_string(fa_status s);
+
+/* Message of the last non-OK status on the calling thread ("" if none);
+ * valid until the next call on that thread. */
+const char* fa_last_error(void);
+
+/* FA_ABI_VERSION of the loaded library. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

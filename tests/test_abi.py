@@ -1,0 +1,140 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol,
+covers every variant, and rejects bad arguments before launching anything.
+
+No call here reaches a launch: every argument set fails a check first, and
+the checks run before any HIP call (the contract of include/fa_mi355x.h).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import flashattention_forward_04_amd as fa
+from flashattention_forward_04_amd import build as fabuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_mi355x.h")
+
+P = 1 << 20  # a 16-byte-aligned stand-in address; never dereferenced here
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        fabuild.build()
+    return fa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(fa.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+        ctypes.cast(getattr(lib, n), ctypes.c_void_p)
+
+
+def test_version_and_status_strings(lib):
+    assert fa.fa_abi_version() == 1
+    assert fa.fa_status_string(fa.FA_OK) == "FA_OK"
+    assert fa.fa_status_string(fa.FA_ERR_INVALID_ARGUMENT) == "FA_ERR_INVALID_ARGUMENT"
+    assert fa.fa_status_string(fa.FA_ERR_UNSUPPORTED) == "FA_ERR_UNSUPPORTED"
+    assert fa.fa_status_string(fa.FA_ERR_HIP) == "FA_ERR_HIP"
+    assert fa.fa_status_string(99) == "FA_ERR_UNKNOWN"
+
+
+def test_variant_table_covers_every_combination(lib):
+    names = [fa.fa_variant_name(i) for i in range(fa.fa_variant_count())]
+    assert None not in names and len(set(names)) == len(names) == 36
+    assert fa.fa_variant_name(len(names)) is None and fa.fa_variant_name(-1) is None
+    for dt in (fa.FA_DTYPE_F32, fa.FA_DTYPE_BF16):
+        for D in (64, 128, 256):
+            for mk in (fa.FA_MASK_NONE, fa.FA_MASK_ADDITIVE, fa.FA_MASK_BOOL):
+                for c in (0, 1):
+                    assert fa.fa_supported(dt, D, mk, c) == 1
+    assert fa.fa_supported(fa.FA_DTYPE_BF16, 96, fa.FA_MASK_NONE, 0) == 0
+    assert fa.fa_supported(7, 64, fa.FA_MASK_NONE, 0) == 0
+
+
+BASE = dict(Q=P, K=P, V=P, mask=None, O=P, L=P, B=1, H_q=4, H_kv=2, qL=16, kL=16, D=64, scale=0.125, causal=0,
+            dtype=fa.FA_DTYPE_BF16, mask_kind=fa.FA_MASK_NONE, hip_stream=None)
+
+BAD = [
+    (dict(B=0), "B must be > 0"),
+    (dict(H_q=0), "H_q must be > 0"),
+    (dict(H_kv=0), "H_kv must be > 0"),
+    (dict(H_q=3), "divisible"),
+    (dict(qL=0), "qL must be > 0"),
+    (dict(kL=-1), "kL must be > 0"),
+    (dict(D=96), "D must be 64, 128 or 256"),
+    (dict(dtype=5), "unknown dtype"),
+    (dict(mask_kind=7, mask=P), "unknown mask kind"),
+    (dict(mask_kind=fa.FA_MASK_ADDITIVE), "mask must be NULL exactly"),
+    (dict(mask=P), "mask must be NULL exactly"),
+    (dict(Q=None), "non-NULL"),
+    (dict(L=None), "non-NULL"),
+    (dict(scale=float("inf")), "finite"),
+    (dict(scale=float("nan")), "finite"),
+    (dict(K=P + 8), "16-byte aligned"),
+    (dict(L=P + 2), "aligned"),
+]
+
+
+@pytest.mark.parametrize("over,msg", BAD, ids=[m for _, m in BAD])
+def test_rejects_bad_arguments(lib, over, msg):
+    a = dict(BASE, **over)
+    st = fa.fa_fwd(a["Q"], a["K"], a["V"], a["mask"], a["O"], a["L"], a["B"], a["H_q"], a["H_kv"], a["qL"],
+                   a["kL"], a["D"], a["scale"], a["causal"], a["dtype"], a["mask_kind"], a["hip_stream"])
+    assert st == fa.FA_ERR_INVALID_ARGUMENT
+    assert msg in fa.fa_last_error()
+
+
+@pytest.mark.parametrize("field,axis,value", [("q", 2, 60), ("o", 0, 4), ("k", 1, -8), ("v", 2, 3)])
+def test_rejects_bad_strides(lib, field, axis, value):
+    st = fa.FaStrides()
+    getattr(st, field)[axis] = value
+    getattr(st, field)[(axis + 1) % 3] = 64  # not an all-zero (default) triple
+    a = BASE
+    rc = fa.fa_fwd_strided(a["Q"], a["K"], a["V"], None, a["O"], a["L"], 1, 4, 2, 16, 16, 64, 0.125, 0,
+                           fa.FA_DTYPE_BF16, fa.FA_MASK_NONE, st, None)
+    assert rc == fa.FA_ERR_INVALID_ARGUMENT
+    assert "stride" in fa.fa_last_error()
+
+
+def test_rejects_negative_mask_stride(lib):
+    st = fa.FaStrides()
+    st.mask[:] = (0, 0, -5)
+    a = BASE
+    rc = fa.fa_fwd_strided(a["Q"], a["K"], a["V"], P, a["O"], a["L"], 1, 4, 2, 16, 16, 64, 0.125, 0,
+                           fa.FA_DTYPE_BF16, fa.FA_MASK_BOOL, st, None)
+    assert rc == fa.FA_ERR_INVALID_ARGUMENT and "mask strides" in fa.fa_last_error()
+
+
+def test_check_raises_with_message(lib):
+    st = fa.fa_fwd(P, P, P, None, P, P, 1, 3, 2, 8, 8, 64, 1.0, 0, 1, 0, None)
+    with pytest.raises(fa.FaError) as e:
+        fa.check(st)
+    assert e.value.status == fa.FA_ERR_INVALID_ARGUMENT and "divisible" in str(e.value)
+
+
+def test_tensor_wrapper_rejects_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        fa.fwd(x, x, x)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    import flashattention_forward_04_amd._binding as b
+    saved = b._lib
+    b._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="not built"):
+            b.load_library(str(tmp_path / "absent.so"))
+    finally:
+        b._lib = saved

@@ -1,0 +1,231 @@
+"""GPU parity: the HIP path against the fp64 oracle, element by element.
+
+Every test calls the library through its C ABI (via the ctypes binding) on
+cuda:0 and compares with the oracle on the same seeded inputs.  Tolerances:
+max abs error on O <= 1e-4 (fp32 outputs) or 2e-2 (bf16 outputs), on L
+<= 1e-3.  The two full-size workloads the oracle cannot finish in seconds
+(causal bf16 8k and the fp32 DiT shape) are checked on sampled rows plus
+properties that hold for every row.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import TOL_L, TOL_O, assert_parity, dtype_name, max_err, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+BF16, F32 = torch.bfloat16, torch.float32
+
+
+def _draw(w):
+    print(f"[case] {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} qL={w.qL} kL={w.kL} D={w.D} {w.dtype} "
+          f"causal={w.causal} mask={w.mask_kind} seed={w.seed}", flush=True)
+    return W.draw(w)
+
+
+def _full_parity(w):
+    q, k, v, mask = _draw(w)
+    O, L, _ = run_gpu(q, k, v, mask, causal=w.causal, scale=w.scale, token_major=w.token_major_out)
+    Oref, Lref = run_oracle(q, k, v, mask, causal=w.causal, scale=w.scale)
+    assert_parity(O, L, Oref, Lref, w.dtype, w.name)
+
+
+@pytest.mark.parametrize("w", [W.C1, W.C2, W.C5], ids=lambda w: w.name)
+def test_config_full(w):
+    _full_parity(w)
+
+
+@pytest.mark.parametrize("w", W.RAGGED, ids=lambda w: w.name)
+def test_ragged(w):
+    _full_parity(w)
+
+
+@pytest.mark.parametrize("w,n_rows", [(W.C3, 1536), (W.C4, 768)], ids=lambda x: getattr(x, "name", str(x)))
+def test_config_full_size_sampled(w, n_rows):
+    """Full-size launch (the configuration the benchmark times); oracle on sampled rows."""
+    q, k, v, mask = _draw(w)
+    O, L, raw = run_gpu(q, k, v, mask, causal=w.causal, scale=w.scale, token_major=w.token_major_out)
+    rows = W.sample_rows(w, n_rows)
+    Oref, Lref = run_oracle(q, k, v, mask, causal=w.causal, scale=w.scale, rows=rows)
+    D = w.D
+    assert_parity(O.reshape(-1, D)[rows], L.reshape(-1)[rows], Oref, Lref, w.dtype, w.name + " sampled")
+    # properties of every row: finite; O inside the per-(b, head) range of V;
+    # s_i0 <= L_i <= scale |q_i| max_j |k_j| + ln kL (key 0 is allowed in every row)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+    grp = w.Hq // w.Hkv
+    vmin = v.double().amin(dim=2).repeat_interleave(grp, dim=1).numpy()[:, :, None, :]
+    vmax = v.double().amax(dim=2).repeat_interleave(grp, dim=1).numpy()[:, :, None, :]
+    slack = TOL_O[w.dtype]
+    assert np.all(O >= vmin - slack) and np.all(O <= vmax + slack), "O outside the range of V"
+    qd, kd = q.double(), k.double().repeat_interleave(grp, dim=1)
+    s0 = (qd * kd[:, :, :1, :]).sum(-1).numpy() * w.scale
+    ub = w.scale * qd.norm(dim=-1).numpy() * kd.norm(dim=-1).amax(dim=2, keepdim=True).numpy() + math.log(w.kL)
+    assert np.all(L >= s0 - TOL_L), "L below the score of key 0"
+    assert np.all(L <= ub + TOL_L), "L above its Cauchy-Schwarz bound"
+    if w.token_major_out:
+        # the output buffer itself is [B, qL, H*D]: out[b, i, h*D + d] = O[b, h, i, d]
+        buf = raw.transpose(1, 2).reshape(w.B, w.qL, w.Hq * w.D).double().cpu().numpy()
+        assert np.array_equal(buf, np.transpose(O, (0, 2, 1, 3)).reshape(w.B, w.qL, w.Hq * w.D))
+
+
+# ---------------------------------------------------------------- edge cases
+
+
+def _rand(shape, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(dtype)
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_head_dims_and_dtypes(dtype, D, causal):
+    q = _rand((1, 4, 200, D), dtype, 1)
+    k = _rand((1, 2, 200, D), dtype, 2)
+    v = _rand((1, 2, 200, D), dtype, 3)
+    scale = 1 / math.sqrt(D)
+    O, L, _ = run_gpu(q, k, v, causal=causal, scale=scale)
+    Oref, Lref = run_oracle(q, k, v, causal=causal, scale=scale)
+    assert_parity(O, L, Oref, Lref, dtype_name(q), f"D={D} {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("kind", ["additive", "bool"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_masks(dtype, kind, causal):
+    D = 64
+    q, k, v = _rand((2, 2, 70, D), dtype, 4), _rand((2, 2, 90, D), dtype, 5), _rand((2, 2, 90, D), dtype, 6)
+    rng = np.random.default_rng(7)
+    masked = W.draw_masked(rng, (2, 2, 70, 90), 0.3)
+    masked[0, 1, 5, :] = True  # a row with no allowed key
+    if kind == "bool":
+        mask = torch.from_numpy((~masked).astype(np.uint8))
+    else:
+        m = rng.standard_normal(masked.shape).astype(np.float32)
+        m[masked] = -np.inf
+        mask = torch.from_numpy(m).to(dtype)
+    O, L, _ = run_gpu(q, k, v, mask, causal=causal, scale=0.125)
+    Oref, Lref = run_oracle(q, k, v, mask, causal=causal, scale=0.125)
+    assert_parity(O, L, Oref, Lref, dtype_name(q), f"{kind} mask causal={causal}")
+    assert np.all(O[0, 1, 5] == 0) and L[0, 1, 5] == 0, "row with no allowed key is not O = 0, L = 0"
+
+
+def test_bool_mask_equals_additive():
+    q, k, v = _rand((1, 2, 64, 128), BF16, 8), _rand((1, 2, 96, 128), BF16, 9), _rand((1, 2, 96, 128), BF16, 10)
+    attend = torch.from_numpy(np.random.default_rng(11).random((1, 2, 64, 96)) < 0.5)
+    attend[..., 3] = True
+    add = torch.zeros(attend.shape, dtype=BF16).masked_fill(~attend, float("-inf"))
+    O1, L1, _ = run_gpu(q, k, v, attend.to(torch.uint8), scale=0.1)
+    O2, L2, _ = run_gpu(q, k, v, add, scale=0.1)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_mask_broadcast_strides():
+    """A [1, 1, qL, kL] mask expanded over batch and heads (stride 0) equals the materialised one."""
+    q, k, v = _rand((2, 3, 40, 64), BF16, 12), _rand((2, 3, 56, 64), BF16, 13), _rand((2, 3, 56, 64), BF16, 14)
+    m = torch.from_numpy(np.where(np.random.default_rng(15).random((1, 1, 40, 56)) < 0.3, -np.inf, 0.0)
+                         .astype(np.float32)).to(BF16)
+    m[..., 0] = 0
+    O1, L1, _ = run_gpu(q, k, v, m.expand(2, 3, 40, 56), scale=0.125)
+    O2, L2, _ = run_gpu(q, k, v, m.expand(2, 3, 40, 56).contiguous(), scale=0.125)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    Oref, Lref = run_oracle(q, k, v, m.expand(2, 3, 40, 56).contiguous(), scale=0.125)
+    assert_parity(O1, L1, Oref, Lref, "bf16", "broadcast mask")
+
+
+@pytest.mark.parametrize("qL,kL", [(1, 1), (1, 300), (300, 1), (64, 500), (500, 64), (129, 33)])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_degenerate_lengths(qL, kL, causal):
+    """Single rows/keys and qL != kL; causal is top-left aligned (row i sees keys 0..i)."""
+    q, k, v = _rand((1, 2, qL, 64), BF16, 16), _rand((1, 1, kL, 64), BF16, 17), _rand((1, 1, kL, 64), BF16, 18)
+    O, L, _ = run_gpu(q, k, v, causal=causal, scale=0.125)
+    Oref, Lref = run_oracle(q, k, v, causal=causal, scale=0.125)
+    assert_parity(O, L, Oref, Lref, "bf16", f"qL={qL} kL={kL} causal={causal}")
+
+
+def test_zero_query_closed_form():
+    """Q = 0: L_i = ln kL (ln(i+1) causal) and O_i = mean of the visible V rows."""
+    kL = 333
+    q = torch.zeros((1, 2, 300, 128), dtype=F32)
+    k, v = _rand((1, 2, kL, 128), F32, 19), _rand((1, 2, kL, 128), F32, 20)
+    O, L, _ = run_gpu(q, k, v, scale=0.3)
+    assert max_err(L, np.full(L.shape, math.log(kL))) <= TOL_L
+    assert max_err(O, np.broadcast_to(v.double().mean(dim=2, keepdim=True).numpy(), O.shape)) <= TOL_O["f32"]
+    O, L, _ = run_gpu(q, k, v, causal=True, scale=0.3)
+    i = np.arange(300)
+    assert max_err(L, np.broadcast_to(np.log(i + 1.0), L.shape)) <= TOL_L
+    csum = np.cumsum(v.double().numpy()[:, :, :300], axis=2) / (i + 1.0)[None, None, :, None]
+    assert max_err(O, csum) <= TOL_O["f32"]
+
+
+def test_dominant_key_closed_form():
+    """One key aligned with the query: O -> that key's V row, L = ln(e^sig + n - 1)."""
+    n, D, jstar, sig = 257, 64, 100, 30.0
+    q = torch.zeros((1, 1, 96, D), dtype=F32)
+    q[..., 0] = 1.0
+    k = _rand((1, 1, n, D), F32, 21)
+    k[..., 0] = 0.0
+    k[0, 0, jstar, 0] = sig / 0.5
+    v = _rand((1, 1, n, D), F32, 22)
+    O, L, _ = run_gpu(q, k, v, scale=0.5)
+    den = math.exp(sig) + n - 1
+    expO = (math.exp(sig) * v[0, 0, jstar].double() + (v[0, 0].double().sum(0) - v[0, 0, jstar].double())) / den
+    assert max_err(L, np.full(L.shape, math.log(den))) <= TOL_L
+    assert max_err(O, np.broadcast_to(expO.numpy(), O.shape)) <= TOL_O["f32"]
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
+def test_causal_first_row(dtype):
+    """Causal row 0 sees only key 0: O_0 = V_0 and L_0 = scale q_0.k_0."""
+    q, k, v = _rand((2, 4, 130, 128), dtype, 23), _rand((2, 2, 130, 128), dtype, 24), _rand((2, 2, 130, 128), dtype, 25)
+    O, L, _ = run_gpu(q, k, v, causal=True, scale=0.09)
+    vr = v.double().repeat_interleave(2, dim=1).numpy()
+    kr = k.double().repeat_interleave(2, dim=1)
+    s00 = 0.09 * (q.double()[:, :, 0] * kr[:, :, 0]).sum(-1).numpy()
+    assert max_err(O[:, :, 0], vr[:, :, 0]) <= (TOL_O[dtype_name(q)] if dtype == BF16 else 1e-6)
+    assert max_err(L[:, :, 0], s00) <= TOL_L
+
+
+def test_gqa_equals_repeated_mha():
+    q, k, v = _rand((1, 8, 100, 64), BF16, 26), _rand((1, 2, 120, 64), BF16, 27), _rand((1, 2, 120, 64), BF16, 28)
+    O1, L1, _ = run_gpu(q, k, v, causal=True, scale=0.125)
+    O2, L2, _ = run_gpu(q, k.repeat_interleave(4, dim=1), v.repeat_interleave(4, dim=1), causal=True, scale=0.125)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_token_major_equals_head_major():
+    q, k, v = _rand((2, 3, 77, 128), F32, 29), _rand((2, 3, 91, 128), F32, 30), _rand((2, 3, 91, 128), F32, 31)
+    O1, L1, raw = run_gpu(q, k, v, scale=0.1, token_major=True)
+    O2, L2, _ = run_gpu(q, k, v, scale=0.1)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    assert raw.stride() == (77 * 3 * 128, 128, 3 * 128, 1)
+
+
+def test_negative_and_zero_scale():
+    q, k, v = _rand((1, 2, 64, 64), BF16, 32), _rand((1, 2, 80, 64), BF16, 33), _rand((1, 2, 80, 64), BF16, 34)
+    for scale in (-0.2, 0.0):
+        O, L, _ = run_gpu(q, k, v, scale=scale)
+        Oref, Lref = run_oracle(q, k, v, scale=scale)
+        assert_parity(O, L, Oref, Lref, "bf16", f"scale={scale}")
+
+
+def test_strided_inputs():
+    """q, k, v as strided views (a packed [B, L, 3, H, D] projection) give the same result."""
+    B, Lx, H, D = 1, 150, 4, 64
+    packed = _rand((B, Lx, 3, H, D), BF16, 35)
+    q, k, v = (packed[:, :, i].transpose(1, 2) for i in range(3))
+    O1, L1, _ = run_gpu(q, k, v, causal=True, scale=0.125)
+    O2, L2, _ = run_gpu(q.contiguous(), k.contiguous(), v.contiguous(), causal=True, scale=0.125)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_repeat_calls_are_deterministic():
+    w = W.C2
+    q, k, v, _ = W.draw(w)
+    O1, L1, _ = run_gpu(q, k, v, causal=True, scale=w.scale)
+    O2, L2, _ = run_gpu(q, k, v, causal=True, scale=w.scale)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
