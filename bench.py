@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--workload", default="causal_bf16_d128_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (a known-size kernel that "
+                         "scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -107,6 +110,16 @@ def main():
 
     import flashattention_forward_04_amd as fa
     import workloads as W
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes device-to-device 3 times")
+        return
 
     w = W.CONFIGS.get(args.workload) or {x.name: x for x in W.RAGGED}[args.workload]
     dev = torch.device("cuda:0")

@@ -26,11 +26,14 @@
 //     documented, so it is not needed here).
 //   * P goes from the S^T accumulator straight into the B operand of the
 //     O^T product: the 8 keys a lane contributes per k-step are a
-//     permutation of a 16-key chunk, and V^T is staged in LDS in that same
-//     permuted key order so the A operand is one 16-byte LDS read per lane.
-//   * K is staged in LDS row-major with a 16-byte pad per row; V is staged
-//     transposed ([D][BN] with the key permutation) from coalesced 16-byte
-//     global loads, packing 4 keys per 8-byte LDS write.
+//     permutation of a 16-key chunk, and the V^T operand is read in that same
+//     key order with two gfx950 transposing LDS reads (ds_read_b64_tr_b16),
+//     so V is staged exactly like K: no VALU transposition.
+//   * K and V are staged in LDS row-major with a padded pitch and an XOR
+//     swizzle of 16-byte chunks (TileLayout) that measures conflict-free on
+//     gfx950 for every access the kernel makes.  Tiles are double-buffered:
+//     tile t+1 is loaded into registers while tile t is computed, so one
+//     barrier per tile suffices and global latency is hidden.
 //   * Causal work-groups are issued longest-first, and key tiles past the
 //     last query row of a work-group are never loaded (forge
 //     flash_attention_mma.metal, the causal j_end bound); a wave whose rows
@@ -40,6 +43,8 @@
 #include "fa_common.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace fa {
 namespace {
@@ -52,40 +57,107 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
-
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
-// Round-to-nearest-even fp32 -> bf16 pair, packed low = a, high = b.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even fp32 -> bf16 pair, packed low = a, high = b (one
+// v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    __bf16 x = (__bf16)a;
-    __bf16 y = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-template <int D, int MASK, bool CAUSAL, int NW, int BN>
-__global__ void __launch_bounds__(NW * 64)
+// Cross-half reductions: lanes l and l^32 hold the two halves of one query
+// row's keys.  v_permlane32_swap(x, x) returns x[l%32] and x[l%32 + 32] in
+// every lane, so one VALU op replaces an LDS-routed shuffle.
+__device__ __forceinline__ float row_max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float row_sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The running max is only moved (and O, l rescaled) when a row's new max
+// exceeds it by more than kRescaleSlack (base-2 units).  Until then P is
+// computed against the stale max, so every P stays <= 2^kRescaleSlack: the
+// result is the same softmax, and the rescale of the accumulator is skipped
+// on almost every tile.
+constexpr float kRescaleSlack = 8.f;
+
+// K and V tiles live in LDS row-major ([BN][D], one key per row) with a
+// padded row pitch: D + 8 elements for K, D + 32 for V.  Measured on gfx950
+// (for D = 64, 128 and 256) these pitches have no bank conflicts for the
+// 16-byte staging writes, the 16-byte K operand reads and the transposing V
+// operand reads, and they keep every operand address a per-lane base plus a
+// compile-time offset.
+template <int P>
+struct TileLayout {
+    static constexpr int PITCH = P;
+    __device__ static __forceinline__ int off(int row, int chunk) { return row * P + chunk * 8; }
+};
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// ds_read_b64_tr_b16: within each 16-lane group, source lane 4e + a reads 4
+// consecutive bf16 of row e (of four rows) at column 4a; destination lane t
+// receives column t of all four rows.  Two of these give a lane the 8 keys
+// of one V^T operand row (head-dim index) without any VALU transposition.
+__device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+}
+
+// NW waves per work-group (32 query rows each), BN keys per tile, WPE waves
+// per SIMD the register allocation must leave room for, PP ping-pong.
+//
+// Each key tile t is handled in two phases per wave: a matrix phase (stage
+// the next tiles into LDS, O^T += V^T P^T for tile t-1, S^T = K Q^T for tile
+// t) and a vector phase (mask, online softmax of tile t into bf16 P).
+// With PP, the eight waves form two groups of four (one wave of each group
+// per SIMD) that run one phase apart, separated by work-group barriers: while
+// group A keeps the matrix cores busy, group B's softmax runs on the vector
+// ALU of the same SIMD, and then they swap.  Each group stages half of every
+// K and V tile, during its matrix phase, into a double-buffered LDS tile
+// that no wave reads in that phase.  Without PP all waves run the phases
+// together (waves of other work-groups on the same SIMD provide overlap).
+template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, bool PP>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fwd_bf16_kernel(const FwdParams p)
 {
     constexpr int NT = NW * 64;
     constexpr int BM = NW * 32;
-    constexpr int KP = D + 8;   // K row pitch in LDS (elements), 16-byte pad
-    constexpr int VP = BN + 8;  // V^T row pitch in LDS (elements), 16-byte pad
-    constexpr int DK = D / 16;  // k-steps of S^T over the head dimension
-    constexpr int NC = BN / 32; // 32-key blocks per key tile
-    constexpr int ND = D / 32;  // 32-wide blocks of O^T along the head dimension
+    using KL = TileLayout<D + 8>;     // K tile layout in LDS
+    using VL = TileLayout<D + 32>;    // V tile layout in LDS
+    constexpr int KTILE = BN * KL::PITCH;
+    constexpr int VTILE = BN * VL::PITCH;
+    constexpr int DK = D / 16;        // k-steps of S^T over the head dimension
+    constexpr int NC = BN / 32;       // 32-key blocks per key tile
+    constexpr int ND = D / 32;        // 32-wide blocks of O^T along the head dimension
+    constexpr int GT = PP ? NT / 2 : NT;        // threads staging a given chunk range
+    constexpr int CH = BN * D / 8;              // 16-byte chunks per tile
+    constexpr int GCH = PP ? CH / 2 : CH;       // chunks per staging group
+    constexpr int SIT = (GCH + GT - 1) / GT;    // chunks per thread per tile
     static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+    static_assert(!PP || NW == 8, "ping-pong pairs two groups of four waves");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * KTILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * VTILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // the wave index is uniform across the wave; saying so keeps the per-wave
+    // branches below (groups, causal skip, masked tiles) scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r32 = lane & 31;
     const int g = lane >> 5;
+    const bool group_b = PP && wave >= NW / 2;
+    const int gtid = group_b ? tid - NT / 2 : tid;   // thread index within the staging group
+    const int gch0 = group_b ? GCH : 0;              // first chunk this group stages
 
     // ---- which (query tile, head, batch) this work-group owns ----
     int id = blockIdx.x;
@@ -96,7 +168,7 @@ fwd_bf16_kernel(const FwdParams p)
     const int qt = CAUSAL ? (p.n_qtiles - 1 - id) : id;  // longest causal tiles first
     const int q0 = qt * BM;
     const int hk = h / p.group;
-    const int wq0 = q0 + wave * 32;
+    const int wq0 = q0 + wave * 32;  // first query row of this wave
     const int qrow = wq0 + r32;
 
     const uint16_t* Qb = (const uint16_t*)p.q + b * p.q_s[0] + h * p.q_s[1];
@@ -119,6 +191,11 @@ fwd_bf16_kernel(const FwdParams p)
 
     const float c2 = p.scale_log2;
     const int kv_end = CAUSAL ? min(p.kL, min(p.qL, q0 + BM)) : p.kL;
+    const int n_tiles = (kv_end + BN - 1) / BN;
+    // this wave needs tiles 0..t_last (a prefix: causal rows never see later keys)
+    int t_last = n_tiles - 1;
+    if (CAUSAL) t_last = min(t_last, (wq0 + 31) / BN);
+    if (wq0 >= p.qL) t_last = -1;
 
     // mask row of this lane (clamped so ragged rows read in bounds)
     const uint8_t* mrow = nullptr;
@@ -131,169 +208,211 @@ fwd_bf16_kernel(const FwdParams p)
     f32x16 o[ND];
 #pragma unroll
     for (int d = 0; d < ND; ++d) o[d] = f32x16{};
-    float m_run = -INFINITY;  // running max, base 2
-    float l_run = 0.f;        // running sum
+    float m_run = -INFINITY;  // running max (base 2) that P is taken against
+    float l_run = 0.f;        // running sum of P
+    f32x16 s[NC];             // scores of the current tile
+    u32x4 pw[NC][2];          // its probabilities, bf16, as O^T B operands
 
-    for (int j0 = 0; j0 < kv_end; j0 += BN) {
-        __syncthreads();  // the previous tile's LDS reads are done
-        // ---- stage K (row-major) ----
-        constexpr int KCH = BN * D / 8;
+    // ---- staging: this thread's chunks of one tile, global -> registers -> LDS ----
+    u32x4 kreg[SIT], vreg[SIT];
+    auto load_part = [&](u32x4 (&r)[SIT], const uint16_t* base, int64_t stride, int j0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int it = 0; it < (KCH + NT - 1) / NT; ++it) {
-            const int c = tid + it * NT;
-            if (KCH % NT != 0 && c >= KCH) break;
-            const int row = c / (D / 8);
-            const int col = c % (D / 8);
-            const int j = j0 + row;
-            u32x4 w = u32x4{0, 0, 0, 0};
-            if (j < p.kL) w = *(const u32x4*)(Kb + (int64_t)j * p.k_s[2] + col * 8);
-            *(u32x4*)(Ks + row * KP + col * 8) = w;
+        for (int it = 0; it < SIT; ++it) {
+            const int c = gch0 + gtid + it * GT;
+            const int j = j0 + c / (D / 8);
+            r[it] = u32x4{0, 0, 0, 0};  // keys past kL stay zero: 0 * garbage never reaches O
+            if ((GCH % GT == 0 || gtid + it * GT < GCH) && j < p.kL)
+                r[it] = *(const u32x4*)(base + (int64_t)j * stride + (c % (D / 8)) * 8);
         }
-        // ---- stage V transposed, keys permuted within each 16-key chunk ----
-        // key quad qd (keys 4qd..4qd+3) lands at position 16(qd/4) + 4*perm[qd%4]
-        // with perm = {0, 2, 1, 3}: a lane in half g then finds keys
-        // {4g..4g+3, 8+4g..8+4g+3} of the chunk as 8 contiguous elements.
-        constexpr int VU = (BN / 4) * (D / 8);
+    };
+    auto store_part = [&](const u32x4 (&r)[SIT], uint16_t* lds, int pitch) __attribute__((always_inline)) {
 #pragma unroll
-        for (int it = 0; it < (VU + NT - 1) / NT; ++it) {
-            const int u = tid + it * NT;
-            if (VU % NT != 0 && u >= VU) break;
-            const int w8 = u % (D / 8);
-            const int qd = u / (D / 8);
-            u32x4 r[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = j0 + 4 * qd + e;
-                r[e] = u32x4{0, 0, 0, 0};
-                if (j < p.kL) r[e] = *(const u32x4*)(Vb + (int64_t)j * p.v_s[2] + w8 * 8);
-            }
-            const int pq = qd & 3;
-            const int pos = 16 * (qd >> 2) + 4 * ((pq == 1) ? 2 : (pq == 2) ? 1 : pq);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int wd = i >> 1;
-                uint32_t lo, hi;
-                if (i & 1) {
-                    lo = (r[0][wd] >> 16) | (r[1][wd] & 0xffff0000u);
-                    hi = (r[2][wd] >> 16) | (r[3][wd] & 0xffff0000u);
-                } else {
-                    lo = (r[0][wd] & 0xffffu) | (r[1][wd] << 16);
-                    hi = (r[2][wd] & 0xffffu) | (r[3][wd] << 16);
-                }
-                *(u32x2*)(Vt + (8 * w8 + i) * VP + pos) = u32x2{lo, hi};
-            }
+        for (int it = 0; it < SIT; ++it) {
+            const int c = gch0 + gtid + it * GT;
+            if (GCH % GT == 0 || gtid + it * GT < GCH) *(u32x4*)(lds + (c / (D / 8)) * pitch + (c % (D / 8)) * 8) = r[it];
         }
-        __syncthreads();
+    };
 
-        // a wave whose rows all precede this key tile has nothing to do here
-        if (CAUSAL && j0 > wq0 + 31) continue;
-
-        // ---- S^T = K Q^T ----
-        f32x16 s[NC];
+    // ---- S^T = K Q^T for the key tile staged at kt ----
+    auto scores = [&](const uint16_t* kt) __attribute__((always_inline)) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) s[c] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < DK; ++ks) {
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                const bf16x8 kop = *(const bf16x8*)(Ks + (32 * c + r32) * KP + 16 * ks + 8 * g);
+                const bf16x8 kop = *(const bf16x8*)(kt + KL::off(32 * c + r32, 2 * ks + g));
                 s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[ks], s[c], 0, 0, 0);
             }
         }
+    };
 
-        // ---- masking: tail keys, causal diagonal, user mask ----
-        const bool fast = (MASK == MASK_NONE) && (j0 + BN <= p.kL) && (!CAUSAL || j0 + BN - 1 <= wq0);
-        float cs = c2;
-        if (!fast) {
-            cs = 1.f;
+    // ---- scores of key tile j0 -> base 2, excluded keys at -inf: keys past
+    // kL, keys after the row (causal), and the user mask ----
+    auto apply_mask = [&](int j0) __attribute__((always_inline)) {
+        if (MASK == MASK_NONE) {
+            // key j0 + 32c + 8rq + 4g + e is allowed iff 32c + 8rq + e <= lim
+            int lim = p.kL - 1;
+            if (CAUSAL) lim = min(lim, qrow);
+            lim -= j0 + 4 * g;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
+            for (int c = 0; c < NC; ++c)
 #pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    const int jb = j0 + 32 * c + 8 * rq + 4 * g;  // first of 4 consecutive keys
-                    float mv[4] = {0.f, 0.f, 0.f, 0.f};
-                    bool mb[4] = {true, true, true, true};
-                    if (MASK == MASK_ADD) {
-                        if (p.mask_vec && jb + 3 < p.kL) {
-                            const u32x2 w = *(const u32x2*)(mrow + 2 * (int64_t)jb);
-                            mv[0] = bf16_bits_to_float(w[0] & 0xffffu);
-                            mv[1] = bf16_bits_to_float(w[0] >> 16);
-                            mv[2] = bf16_bits_to_float(w[1] & 0xffffu);
-                            mv[3] = bf16_bits_to_float(w[1] >> 16);
-                        } else {
+                for (int r = 0; r < 16; ++r)
+                    s[c][r] = (32 * c + 8 * (r >> 2) + (r & 3) <= lim) ? s[c][r] * c2 : -INFINITY;
+            return;
+        }
 #pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (jb + e < p.kL)
-                                    mv[e] = bf16_bits_to_float(((const uint16_t*)mrow)[jb + e]);
-                        }
-                    } else if (MASK == MASK_BOOL) {
-                        if (p.mask_vec && jb + 3 < p.kL) {
-                            const uint32_t w = *(const uint32_t*)(mrow + jb);
+        for (int c = 0; c < NC; ++c) {
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) mb[e] = ((w >> (8 * e)) & 0xffu) != 0;
-                        } else {
+            for (int rq = 0; rq < 4; ++rq) {
+                const int jb = j0 + 32 * c + 8 * rq + 4 * g;  // first of 4 consecutive keys
+                float mv[4] = {0.f, 0.f, 0.f, 0.f};
+                bool mb[4] = {true, true, true, true};
+                if (MASK == MASK_ADD) {
+                    if (p.mask_vec && jb + 3 < p.kL) {
+                        const u32x2 w = *(const u32x2*)(mrow + 2 * (int64_t)jb);
+                        mv[0] = bf16_bits_to_float(w[0] & 0xffffu);
+                        mv[1] = bf16_bits_to_float(w[0] >> 16);
+                        mv[2] = bf16_bits_to_float(w[1] & 0xffffu);
+                        mv[3] = bf16_bits_to_float(w[1] >> 16);
+                    } else {
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) mb[e] = (jb + e < p.kL) ? (mrow[jb + e] != 0) : false;
-                        }
+                        for (int e = 0; e < 4; ++e)
+                            if (jb + e < p.kL) mv[e] = bf16_bits_to_float(((const uint16_t*)mrow)[jb + e]);
                     }
+                } else {
+                    if (p.mask_vec && jb + 3 < p.kL) {
+                        const uint32_t w = *(const uint32_t*)(mrow + jb);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int j = jb + e;
-                        bool ok = (j < p.kL) && mb[e];
-                        if (CAUSAL) ok = ok && (j <= qrow);
-                        float t = s[c][4 * rq + e] * c2;
-                        if (MASK == MASK_ADD) t = __builtin_fmaf(mv[e], kLog2e, t);
-                        s[c][4 * rq + e] = ok ? t : -INFINITY;
+                        for (int e = 0; e < 4; ++e) mb[e] = ((w >> (8 * e)) & 0xffu) != 0;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) mb[e] = (jb + e < p.kL) ? (mrow[jb + e] != 0) : false;
                     }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = jb + e;
+                    bool ok = (j < p.kL) && mb[e];
+                    if (CAUSAL) ok = ok && (j <= qrow);
+                    float x = s[c][4 * rq + e] * c2;
+                    if (MASK == MASK_ADD) x = __builtin_fmaf(mv[e], kLog2e, x);
+                    s[c][4 * rq + e] = ok ? x : -INFINITY;
                 }
             }
         }
+    };
 
-        // ---- online softmax for this lane's row ----
+    // ---- online softmax of s (raw when cs == c2, base 2 when cs == 1) into pw ----
+    auto softmax = [&](float cs) __attribute__((always_inline)) {
         float mx = s[0][0];
 #pragma unroll
         for (int c = 0; c < NC; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c][r]);
-        mx = fmaxf(mx, xor32(mx));
-        const float m_new = fmaxf(m_run, mx * cs);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
-        float rs = 0.f;
+        const float m_tile = row_max_halves(mx) * cs;
+        if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
+            const float m_new = fmaxf(m_run, m_tile);
+            if (m_run != -INFINITY && m_new != m_run) {
+                const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= corr;
+#pragma unroll
+                for (int d = 0; d < ND; ++d) o[d] *= corr;
+            }
+            m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        // the row sum is taken in fp32 before P is rounded to bf16: L must
+        // stay within 1e-3 even for rows that see only a few keys
+        float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
         for (int c = 0; c < NC; ++c)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][r], cs, -m_use));
-                s[c][r] = e;
-                rs += e;
-            }
-        rs += xor32(rs);
-        l_run = l_run * corr + rs;
-        m_run = m_new;
+            for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int d = 0; d < ND; ++d) o[d] *= corr;
+                for (int e = 0; e < 4; ++e) {
+                    const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][8 * hh + 2 * e], cs, -m_use));
+                    const float z = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][8 * hh + 2 * e + 1], cs, -m_use));
+                    pw[c][hh][e] = pack_bf16x2(a, z);
+                    rs0 += a;
+                    rs1 += z;
+                }
+        l_run += row_sum_halves(rs0 + rs1);
+    };
 
-        // ---- O^T += V^T P^T ----
+    // ---- O^T += V^T P^T for the value tile staged at vt ----
+    auto pv = [&](const uint16_t* vt) __attribute__((always_inline)) {
+        const int lt = lane & 15;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                u32x4 pw;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(s[c][8 * hh + 2 * e], s[c][8 * hh + 2 * e + 1]);
-                const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+                const bf16x8 pf = __builtin_bit_cast(bf16x8, pw[c][hh]);
                 const int kidx = 2 * c + hh;
 #pragma unroll
                 for (int d = 0; d < ND; ++d) {
-                    const bf16x8 vop = *(const bf16x8*)(Vt + (32 * d + r32) * VP + 16 * kidx + 8 * g);
+                    // lane l: head-dim column 32d + l%32, keys 16kidx + 4g + {0..3}
+                    // and 16kidx + 8 + 4g + {0..3}, the order P was packed in
+                    const int col = 32 * d + 16 * ((lane >> 4) & 1) + 4 * (lt & 3);
+                    const int row0 = 16 * kidx + 4 * g + (lt >> 2);
+                    const i16x4 v0 = lds_read_tr(vt + VL::off(row0, 0) + col);
+                    const i16x4 v1 = lds_read_tr(vt + VL::off(row0 + 8, 0) + col);
+                    const bf16x8 vop =
+                        __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
                     o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pf, o[d], 0, 0, 0);
                 }
             }
         }
-    }
+    };
 
-    // ---- epilogue: O = O / l, L = m ln2 + ln l (O = 0, L = 0 if no key) ----
+    auto vector_phase = [&](int t) __attribute__((always_inline)) {
+        const int j0 = t * BN;
+        const bool masked = (MASK != MASK_NONE) || (j0 + BN > p.kL) || (CAUSAL && j0 + BN - 1 > wq0);
+        if (masked) {
+            apply_mask(j0);
+            softmax(1.f);
+        } else {
+            softmax(c2);
+        }
+    };
+
+    // ---- prologue: K tile 0 into LDS (all threads), registers <- K tile 1, V tile 0 ----
+    {
+        constexpr int PIT = (CH + NT - 1) / NT;
+#pragma unroll
+        for (int it = 0; it < PIT; ++it) {
+            const int c = tid + it * NT;
+            if (CH % NT == 0 || c < CH) {
+                const int j = c / (D / 8);
+                u32x4 w = u32x4{0, 0, 0, 0};
+                if (j < p.kL) w = *(const u32x4*)(Kb + (int64_t)j * p.k_s[2] + (c % (D / 8)) * 8);
+                *(u32x4*)(Ks + KL::off(j, c % (D / 8))) = w;
+            }
+        }
+    }
+    if (n_tiles > 1) load_part(kreg, Kb, p.k_s[2], BN);
+    load_part(vreg, Vb, p.v_s[2], 0);
+    __syncthreads();
+    if (group_b) __syncthreads();  // group B trails group A by one phase
+
+    for (int t = 0;; ++t) {
+        // ---- matrix phase of tile t: stage K t+1 and V t, P V of t-1, S of t ----
+        if (t + 1 < n_tiles) store_part(kreg, Ks + ((t + 1) & 1) * KTILE, KL::PITCH);
+        if (t < n_tiles) store_part(vreg, Vs + (t & 1) * VTILE, VL::PITCH);
+        if (t + 2 < n_tiles) load_part(kreg, Kb, p.k_s[2], (t + 2) * BN);
+        if (t + 1 < n_tiles) load_part(vreg, Vb, p.v_s[2], (t + 1) * BN);
+        if (t >= 1 && t - 1 <= t_last) pv(Vs + ((t - 1) & 1) * VTILE);
+        if (t < n_tiles && t <= t_last) scores(Ks + (t & 1) * KTILE);
+        if (t == n_tiles) break;
+        __syncthreads();
+        // ---- vector phase of tile t ----
+        if (t <= t_last) vector_phase(t);
+        if (PP) __syncthreads();
+    }
+    if (PP && !group_b) __syncthreads();  // matches group B's extra leading barrier
+
+    // ---- epilogue: O = O / l, L = (m + log2 l) ln2 (O = 0, L = 0 if no key) ----
     if (qrow < p.qL) {
         const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
         uint16_t* orow = (uint16_t*)p.o + b * p.o_s[0] + h * p.o_s[1] + (int64_t)qrow * p.o_s[2];
@@ -313,35 +432,62 @@ fwd_bf16_kernel(const FwdParams p)
     }
 }
 
-template <int D, int MASK, bool CAUSAL, int NW, int BN>
+template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, bool PP>
 hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
 {
     const dim3 grid((unsigned)p.n_qtiles * p.Hq * p.B);
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN>), grid, dim3(NW * 64), 0, st, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, PP>), grid, dim3(NW * 64), 0, st, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
-#define FA_BF16_VARIANT(D, MASK, CAUSAL, NW, BN, NAME) \
-    {NAME, 1, D, MASK, CAUSAL, NW * 32, &launch_bf16<D, MASK, CAUSAL, NW, BN>}
+// Launch shapes per head dimension and mask use: waves per work-group, keys
+// per tile, waves per SIMD, ping-pong.  Eight waves of 32
+// rows share each staged K/V tile where the registers allow two waves per
+// SIMD; at D = 256 the output accumulator alone is 128 registers per lane, so
+// that size runs four waves at one per SIMD.  Overridable at build time for
+// tuning sweeps.
+#ifndef FA_BF16_D64_CFG
+#define FA_BF16_D64_CFG 4, 64, 2, false
+#endif
+#ifndef FA_BF16_D64_MASKED_CFG
+#define FA_BF16_D64_MASKED_CFG 4, 64, 2, false
+#endif
+#ifndef FA_BF16_D128_CFG
+#define FA_BF16_D128_CFG 8, 64, 2, false
+#endif
+#ifndef FA_BF16_D128_MASKED_CFG
+#define FA_BF16_D128_MASKED_CFG 8, 64, 2, false
+#endif
+#ifndef FA_BF16_D256_CFG
+#define FA_BF16_D256_CFG 4, 32, 1, false
+#endif
+#ifndef FA_BF16_D256_MASKED_CFG
+#define FA_BF16_D256_MASKED_CFG 4, 32, 1, false
+#endif
 
-#define FA_BF16_FOR_D(D, NW, BN)                                                          \
-    FA_BF16_VARIANT(D, MASK_NONE, false, NW, BN, "fwd_bf16_d" #D "_nomask"),              \
-    FA_BF16_VARIANT(D, MASK_NONE, true, NW, BN, "fwd_bf16_d" #D "_nomask_causal"),        \
-    FA_BF16_VARIANT(D, MASK_ADD, false, NW, BN, "fwd_bf16_d" #D "_additive"),             \
-    FA_BF16_VARIANT(D, MASK_ADD, true, NW, BN, "fwd_bf16_d" #D "_additive_causal"),       \
-    FA_BF16_VARIANT(D, MASK_BOOL, false, NW, BN, "fwd_bf16_d" #D "_bool"),                \
-    FA_BF16_VARIANT(D, MASK_BOOL, true, NW, BN, "fwd_bf16_d" #D "_bool_causal")
+#define FA_BF16_VARIANT(D, MASK, CAUSAL, NAME, NW, BN, WPE, PP) \
+    {NAME, 1, D, MASK, CAUSAL, NW * 32, &launch_bf16<D, MASK, CAUSAL, NW, BN, WPE, PP>}
+// expands a CFG macro into separate arguments before FA_BF16_VARIANT sees them
+#define FA_BF16_VARIANT_CFG(...) FA_BF16_VARIANT(__VA_ARGS__)
+
+#define FA_BF16_FOR_D(D, CFG, MCFG)                                                       \
+    FA_BF16_VARIANT_CFG(D, MASK_NONE, false, "fwd_bf16_d" #D "_nomask", CFG),             \
+    FA_BF16_VARIANT_CFG(D, MASK_NONE, true, "fwd_bf16_d" #D "_nomask_causal", CFG),       \
+    FA_BF16_VARIANT_CFG(D, MASK_ADD, false, "fwd_bf16_d" #D "_additive", MCFG),           \
+    FA_BF16_VARIANT_CFG(D, MASK_ADD, true, "fwd_bf16_d" #D "_additive_causal", MCFG),     \
+    FA_BF16_VARIANT_CFG(D, MASK_BOOL, false, "fwd_bf16_d" #D "_bool", MCFG),              \
+    FA_BF16_VARIANT_CFG(D, MASK_BOOL, true, "fwd_bf16_d" #D "_bool_causal", MCFG)
 
 // Host-only accessor: a namespace-scope const table would also be emitted
 // for the device, where the launch functions do not exist.
 const Variant* variants_bf16(int* n)
 {
     static const Variant table[] = {
-    FA_BF16_FOR_D(64, 4, 64),
-    FA_BF16_FOR_D(128, 4, 64),
-    FA_BF16_FOR_D(256, 4, 32),
+    FA_BF16_FOR_D(64, FA_BF16_D64_CFG, FA_BF16_D64_MASKED_CFG),
+    FA_BF16_FOR_D(128, FA_BF16_D128_CFG, FA_BF16_D128_MASKED_CFG),
+    FA_BF16_FOR_D(256, FA_BF16_D256_CFG, FA_BF16_D256_MASKED_CFG),
 };
     *n = (int)(sizeof(table) / sizeof(table[0]));
     return table;
