@@ -34,8 +34,150 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "flashattention_forward_04_amd", "csrc")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources: a recorded traffic figure is only
+    reported while the kernels it was measured on are unchanged."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(w):
+    """HBM bytes per launch recorded by --summarize for workload w, or None."""
+    path = os.path.join(PROFILES, f"{w.name}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _read_counter_csv(path, counter):
+    """{kernel name: [per-dispatch values]} for one counter of a rocprofv3 CSV."""
+    import csv
+
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize(prof_dir, w, commands):
+    """Write profiles/<workload>.md (+ .traffic.json) from rocprofv3 outputs.
+
+    prof_dir holds the outputs of: a --kernel-trace --stats run (trace/),
+    FETCH_SIZE and WRITE_SIZE runs of the workload (fetch/, write/), and the
+    same two counters on a device copy of known size (copyf/, copyw/).
+    The counters are KiB per dispatch; each is scaled by (known copy bytes /
+    what the counter reads for that copy).
+    """
+    import csv
+    import glob
+
+    def one(pattern):
+        hits = glob.glob(os.path.join(prof_dir, pattern))
+        if not hits:
+            raise FileNotFoundError(os.path.join(prof_dir, pattern))
+        return hits[0]
+
+    stats = list(csv.DictReader(open(one("trace/*kernel_stats.csv"))))
+    fa_rows = [r for r in stats if "fa::" in r["Name"]]
+    if not fa_rows:
+        raise RuntimeError("no fa:: kernel in the kernel-trace stats")
+    k = max(fa_rows, key=lambda r: float(r["TotalDurationNs"]))
+    avg_us = float(k["AverageNs"]) / 1e3
+    # the timed steps are the last `steps` dispatches of the kernel (the
+    # earlier ones are bench.py's warm-up calls)
+    disp = [r for r in csv.DictReader(open(one("trace/*kernel_trace.csv"))) if r["Kernel_Name"] == k["Name"]]
+    disp.sort(key=lambda r: int(r["Start_Timestamp"]))
+    timed = disp[-commands["steps"]:]
+    timed_us = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in timed) / len(timed) / 1e3
+    copy_bytes = commands["copy_mib"] << 20
+
+    def scale(counter, sub_run, sub_copy):
+        vals = _read_counter_csv(one(f"{sub_run}/*counter_collection.csv"), counter)
+        kv = [v for n, v in vals.items() if "fa::" in n]
+        per = sum(kv[0]) / len(kv[0]) * 1024.0
+        cvals = _read_counter_csv(one(f"{sub_copy}/*counter_collection.csv"), counter)
+        cv = [v for n, v in cvals.items() if "copyBuffer" in n]
+        cper = sum(cv[0]) / len(cv[0]) * 1024.0
+        return per, cper, copy_bytes / cper
+
+    f_raw, f_copy, f_factor = scale("FETCH_SIZE", "fetch", "copyf")
+    w_raw, w_copy, w_factor = scale("WRITE_SIZE", "write", "copyw")
+    fetch, write = f_raw * f_factor, w_raw * w_factor
+    flops = w.flops()
+    alg = algorithmic_bytes(w)
+    os.makedirs(PROFILES, exist_ok=True)
+    rec = {"workload": w.name, "kernel": k["Name"], "calls": int(k["Calls"]), "avg_us": avg_us,
+           "timed_steps": len(timed), "timed_avg_us": timed_us,
+           "min_us": float(k["MinNs"]) / 1e3, "max_us": float(k["MaxNs"]) / 1e3,
+           "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+           "hbm_bytes_per_launch": fetch + write, "algorithmic_bytes": alg,
+           "fetch_scale": f_factor, "write_scale": w_factor,
+           "source_sha256": kernel_source_hash()}
+    with open(os.path.join(PROFILES, f"{w.name}.traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    peak = PEAK_TFLOPS[w.dtype]
+    lines = [
+        f"# {k['Name']} -- {w.name}",
+        "",
+        f"Workload: {w.note}; B={w.B} H_q={w.Hq} H_kv={w.Hkv} qL={w.qL} kL={w.kL} D={w.D} {w.dtype} "
+        f"causal={w.causal} mask={w.mask_kind}.  FLOP per launch {flops:.4g}; algorithmic bytes {alg:.4g}.",
+        "",
+        "## Kernel duration (rocprofv3 --kernel-trace --stats)",
+        "",
+        "```",
+        commands["trace"],
+        "```",
+        "",
+        f"| calls | avg us (all) | avg us (last {len(timed)} = timed steps) | min us | max us | "
+        f"TFLOP/s at timed avg | % of {peak} TFLOP/s |",
+        "|---|---|---|---|---|---|---|",
+        f"| {k['Calls']} | {avg_us:.1f} | {timed_us:.1f} | {rec['min_us']:.1f} | {rec['max_us']:.1f} | "
+        f"{flops / (timed_us * 1e-6) / 1e12:.1f} | {100 * flops / (timed_us * 1e-6) / 1e12 / peak:.1f} |",
+        "",
+        "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE; KiB per dispatch)",
+        "",
+        "```",
+        commands["fetch"],
+        commands["write"],
+        commands["copyf"],
+        commands["copyw"],
+        "```",
+        "",
+        f"Copy calibration: a device copy of {copy_bytes} bytes reads FETCH_SIZE = {f_copy:.4g} B "
+        f"(scale {f_factor:.3f}) and WRITE_SIZE = {w_copy:.4g} B (scale {w_factor:.3f}).",
+        "",
+        "| counter | raw bytes/launch | scaled bytes/launch |",
+        "|---|---|---|",
+        f"| FETCH_SIZE | {f_raw:.4g} | {fetch:.4g} |",
+        f"| WRITE_SIZE | {w_raw:.4g} | {write:.4g} |",
+        f"| total | | {fetch + write:.4g} ({(fetch + write) / alg:.2f}x algorithmic) |",
+        "",
+        f"Kernel source sha256 {rec['source_sha256'][:16]}...; bench.py reports this traffic only while it matches.",
+        "",
+    ]
+    with open(os.path.join(PROFILES, f"{w.name}.md"), "w") as f:
+        f.write("\n".join(lines))
+    log(f"wrote profiles/{w.name}.md and .traffic.json")
 
 
 def algorithmic_bytes(w) -> int:
@@ -99,17 +241,40 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (a known-size kernel that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
+    ap.add_argument("--summarize", metavar="PROF_DIR", default=None,
+                    help="only write profiles/<workload>.md from rocprofv3 outputs under PROF_DIR, then exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               f"(the attention path needs no cross-GPU exchange; see the sharding notes in the docs).",
               file=sys.stderr)
         sys.exit(2)
 
+    import workloads as W
+
+    if args.summarize:
+        w = W.CONFIGS.get(args.workload) or {x.name: x for x in W.RAGGED}[args.workload]
+        base = f"--workload {w.name}" if w.name != "causal_bf16_d128_8k" else ""
+        cmds = {
+            "copy_mib": 1024,
+            "steps": args.steps,
+            "trace": f"rocprofv3 --kernel-trace --stats --output-format csv -d {args.summarize}/trace -o trace -- "
+                     f"python3 bench.py --steps {args.steps} --warmup {args.warmup} {base}".strip(),
+            "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {args.summarize}/fetch -o fetch -- "
+                     f"python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline {base}".strip(),
+            "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {args.summarize}/write -o write -- "
+                     f"python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline {base}".strip(),
+            "copyf": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {args.summarize}/copyf -o copyf -- "
+                     "python3 bench.py --copy-calibration-mib 1024",
+            "copyw": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {args.summarize}/copyw -o copyw -- "
+                     "python3 bench.py --copy-calibration-mib 1024",
+        }
+        summarize(args.summarize, w, cmds)
+        return
+
     import torch
 
     import flashattention_forward_04_amd as fa
-    import workloads as W
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -193,7 +358,7 @@ def main():
                    "flop_per_step": flops},
         "mfma_peak_frac": round(achieved / peak, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4), "traffic": recorded_traffic(w),
                      "kernel_avg_us": round(kern_avg_ms * 1e3, 2)},
         "cpu_baseline": cpu,
     }

@@ -32,6 +32,16 @@ struct FwdParams {
 
 enum MaskKind { MASK_NONE = 0, MASK_ADD = 1, MASK_BOOL = 2 };
 
+// Work-groups are dispatched round-robin over the 8 XCDs (each with its own
+// L2): work-group i runs on XCD i % 8.  Within the H_q consecutive
+// work-groups of one (query tile, batch), slot i gets query head
+// (i % 8) * (H_q / 8) + i / 8, so each XCD receives H_q / 8 consecutive
+// heads -- whole GQA groups when H_kv >= 8 -- and re-reads their K/V tiles
+// from its own L2.  Other head counts keep the plain order.
+__device__ __forceinline__ int head_of(int slot, int Hq) {
+    return (Hq % 8 == 0) ? (slot % 8) * (Hq / 8) + slot / 8 : slot;
+}
+
 // One compiled variant: its launch function and shape facts the host needs.
 typedef hipError_t (*LaunchFn)(const FwdParams&, hipStream_t);
 

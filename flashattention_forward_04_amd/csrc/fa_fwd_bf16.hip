@@ -113,19 +113,18 @@ __device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
 }
 
 // NW waves per work-group (32 query rows each), BN keys per tile, WPE waves
-// per SIMD the register allocation must leave room for, PP ping-pong.
+// per SIMD the register allocation must leave room for, PIPE pipelining.
 //
-// Each key tile t is handled in two phases per wave: a matrix phase (stage
-// the next tiles into LDS, O^T += V^T P^T for tile t-1, S^T = K Q^T for tile
-// t) and a vector phase (mask, online softmax of tile t into bf16 P).
-// With PP, the eight waves form two groups of four (one wave of each group
-// per SIMD) that run one phase apart, separated by work-group barriers: while
-// group A keeps the matrix cores busy, group B's softmax runs on the vector
-// ALU of the same SIMD, and then they swap.  Each group stages half of every
-// K and V tile, during its matrix phase, into a double-buffered LDS tile
-// that no wave reads in that phase.  Without PP all waves run the phases
-// together (waves of other work-groups on the same SIMD provide overlap).
-template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, bool PP>
+// On gfx950 a wave's matrix-core instructions overlap with its own
+// independent vector instructions, but hardly with another wave's on the
+// same SIMD (measured).  With PIPE each wave therefore issues the products
+// for the scores of key tile t+1 in the same instruction stream as the
+// softmax and P V of tile t, so the matrix cores keep running through the
+// softmax.  That puts the K tile one step ahead of the V tile: iteration t
+// reads K tile t+1 and V tile t and stages K tile t+2 and V tile t+1 into
+// the other buffers; the barrier that ends iteration t-1 separates every
+// reuse.  Without PIPE a tile's scores, softmax and P V run back to back.
+template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, bool PIPE>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fwd_bf16_kernel(const FwdParams p)
 {
@@ -138,12 +137,9 @@ fwd_bf16_kernel(const FwdParams p)
     constexpr int DK = D / 16;        // k-steps of S^T over the head dimension
     constexpr int NC = BN / 32;       // 32-key blocks per key tile
     constexpr int ND = D / 32;        // 32-wide blocks of O^T along the head dimension
-    constexpr int GT = PP ? NT / 2 : NT;        // threads staging a given chunk range
-    constexpr int CH = BN * D / 8;              // 16-byte chunks per tile
-    constexpr int GCH = PP ? CH / 2 : CH;       // chunks per staging group
-    constexpr int SIT = (GCH + GT - 1) / GT;    // chunks per thread per tile
+    constexpr int CH = BN * D / 8;    // 16-byte chunks per tile
+    constexpr int SIT = (CH + NT - 1) / NT;  // chunks per thread per tile
     static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
-    static_assert(!PP || NW == 8, "ping-pong pairs two groups of four waves");
 
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * KTILE];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * VTILE];
@@ -151,17 +147,14 @@ fwd_bf16_kernel(const FwdParams p)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // the wave index is uniform across the wave; saying so keeps the per-wave
-    // branches below (groups, causal skip, masked tiles) scalar
+    // branches below (causal skip, masked tiles) scalar
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r32 = lane & 31;
     const int g = lane >> 5;
-    const bool group_b = PP && wave >= NW / 2;
-    const int gtid = group_b ? tid - NT / 2 : tid;   // thread index within the staging group
-    const int gch0 = group_b ? GCH : 0;              // first chunk this group stages
 
     // ---- which (query tile, head, batch) this work-group owns ----
     int id = blockIdx.x;
-    const int h = id % p.Hq;
+    const int h = head_of(id % p.Hq, p.Hq);
     id /= p.Hq;
     const int b = id % p.B;
     id /= p.B;
@@ -210,31 +203,28 @@ fwd_bf16_kernel(const FwdParams p)
     for (int d = 0; d < ND; ++d) o[d] = f32x16{};
     float m_run = -INFINITY;  // running max (base 2) that P is taken against
     float l_run = 0.f;        // running sum of P
-    f32x16 s[NC];             // scores of the current tile
-    u32x4 pw[NC][2];          // its probabilities, bf16, as O^T B operands
 
-    // ---- staging: this thread's chunks of one tile, global -> registers -> LDS ----
-    u32x4 kreg[SIT], vreg[SIT];
+    // ---- staging: this thread's chunks of a tile, global -> registers -> LDS ----
     auto load_part = [&](u32x4 (&r)[SIT], const uint16_t* base, int64_t stride, int j0) __attribute__((always_inline)) {
 #pragma unroll
         for (int it = 0; it < SIT; ++it) {
-            const int c = gch0 + gtid + it * GT;
+            const int c = tid + it * NT;
             const int j = j0 + c / (D / 8);
             r[it] = u32x4{0, 0, 0, 0};  // keys past kL stay zero: 0 * garbage never reaches O
-            if ((GCH % GT == 0 || gtid + it * GT < GCH) && j < p.kL)
+            if ((CH % NT == 0 || c < CH) && j < p.kL)
                 r[it] = *(const u32x4*)(base + (int64_t)j * stride + (c % (D / 8)) * 8);
         }
     };
     auto store_part = [&](const u32x4 (&r)[SIT], uint16_t* lds, int pitch) __attribute__((always_inline)) {
 #pragma unroll
         for (int it = 0; it < SIT; ++it) {
-            const int c = gch0 + gtid + it * GT;
-            if (GCH % GT == 0 || gtid + it * GT < GCH) *(u32x4*)(lds + (c / (D / 8)) * pitch + (c % (D / 8)) * 8) = r[it];
+            const int c = tid + it * NT;
+            if (CH % NT == 0 || c < CH) *(u32x4*)(lds + (c / (D / 8)) * pitch + (c % (D / 8)) * 8) = r[it];
         }
     };
 
     // ---- S^T = K Q^T for the key tile staged at kt ----
-    auto scores = [&](const uint16_t* kt) __attribute__((always_inline)) {
+    auto scores = [&](f32x16 (&s)[NC], const uint16_t* kt) __attribute__((always_inline)) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) s[c] = f32x16{};
 #pragma unroll
@@ -249,7 +239,7 @@ fwd_bf16_kernel(const FwdParams p)
 
     // ---- scores of key tile j0 -> base 2, excluded keys at -inf: keys past
     // kL, keys after the row (causal), and the user mask ----
-    auto apply_mask = [&](int j0) __attribute__((always_inline)) {
+    auto apply_mask = [&](f32x16 (&s)[NC], int j0) __attribute__((always_inline)) {
         if (MASK == MASK_NONE) {
             // key j0 + 32c + 8rq + 4g + e is allowed iff 32c + 8rq + e <= lim
             int lim = p.kL - 1;
@@ -304,8 +294,9 @@ fwd_bf16_kernel(const FwdParams p)
         }
     };
 
-    // ---- online softmax of s (raw when cs == c2, base 2 when cs == 1) into pw ----
-    auto softmax = [&](float cs) __attribute__((always_inline)) {
+    // ---- online softmax of s (raw when cs == c2, base 2 when cs == 1), then
+    // O^T += V^T P^T from the value tile staged at vt ----
+    auto softmax_pv = [&](f32x16 (&s)[NC], float cs, const uint16_t* vt) __attribute__((always_inline)) {
         float mx = s[0][0];
 #pragma unroll
         for (int c = 0; c < NC; ++c)
@@ -326,29 +317,21 @@ fwd_bf16_kernel(const FwdParams p)
         // the row sum is taken in fp32 before P is rounded to bf16: L must
         // stay within 1e-3 even for rows that see only a few keys
         float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][8 * hh + 2 * e], cs, -m_use));
-                    const float z = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][8 * hh + 2 * e + 1], cs, -m_use));
-                    pw[c][hh][e] = pack_bf16x2(a, z);
-                    rs0 += a;
-                    rs1 += z;
-                }
-        l_run += row_sum_halves(rs0 + rs1);
-    };
-
-    // ---- O^T += V^T P^T for the value tile staged at vt ----
-    auto pv = [&](const uint16_t* vt) __attribute__((always_inline)) {
         const int lt = lane & 15;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const bf16x8 pf = __builtin_bit_cast(bf16x8, pw[c][hh]);
+                u32x4 pw;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][8 * hh + 2 * e], cs, -m_use));
+                    const float z = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][8 * hh + 2 * e + 1], cs, -m_use));
+                    pw[e] = pack_bf16x2(a, z);
+                    rs0 += a;
+                    rs1 += z;
+                }
+                const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
                 const int kidx = 2 * c + hh;
 #pragma unroll
                 for (int d = 0; d < ND; ++d) {
@@ -364,53 +347,86 @@ fwd_bf16_kernel(const FwdParams p)
                 }
             }
         }
+        l_run += row_sum_halves(rs0 + rs1);
     };
 
-    auto vector_phase = [&](int t) __attribute__((always_inline)) {
+    // softmax and P V of tile t with its scores in s
+    auto finish_tile = [&](f32x16 (&s)[NC], int t, const uint16_t* vt) __attribute__((always_inline)) {
         const int j0 = t * BN;
         const bool masked = (MASK != MASK_NONE) || (j0 + BN > p.kL) || (CAUSAL && j0 + BN - 1 > wq0);
         if (masked) {
-            apply_mask(j0);
-            softmax(1.f);
+            apply_mask(s, j0);
+            softmax_pv(s, 1.f, vt);
         } else {
-            softmax(c2);
+            softmax_pv(s, c2, vt);
         }
     };
 
-    // ---- prologue: K tile 0 into LDS (all threads), registers <- K tile 1, V tile 0 ----
-    {
-        constexpr int PIT = (CH + NT - 1) / NT;
-#pragma unroll
-        for (int it = 0; it < PIT; ++it) {
-            const int c = tid + it * NT;
-            if (CH % NT == 0 || c < CH) {
-                const int j = c / (D / 8);
-                u32x4 w = u32x4{0, 0, 0, 0};
-                if (j < p.kL) w = *(const u32x4*)(Kb + (int64_t)j * p.k_s[2] + (c % (D / 8)) * 8);
-                *(u32x4*)(Ks + KL::off(j, c % (D / 8))) = w;
+    u32x4 kreg[SIT], vreg[SIT];
+    if (PIPE) {
+        f32x16 sa[NC], sb[NC];
+        // ---- prologue: K tiles 0, 1 and V tile 0 in LDS; scores of tile 0 ----
+        load_part(kreg, Kb, p.k_s[2], 0);
+        load_part(vreg, Vb, p.v_s[2], 0);
+        store_part(kreg, Ks, KL::PITCH);
+        store_part(vreg, Vs, VL::PITCH);
+        load_part(kreg, Kb, p.k_s[2], BN);
+        store_part(kreg, Ks + KTILE, KL::PITCH);
+        __syncthreads();
+        if (t_last >= 0) scores(sa, Ks);
+        load_part(kreg, Kb, p.k_s[2], 2 * BN);
+        load_part(vreg, Vb, p.v_s[2], BN);
+        __syncthreads();  // K tile 0's buffer is restaged in iteration 0
+
+        // iteration t: stage K t+2 and V t+1, scores of t+1 into s_next, and
+        // softmax + P V of tile t from s_cur
+        auto iteration = [&](int t, f32x16 (&s_cur)[NC], f32x16 (&s_next)[NC]) __attribute__((always_inline)) {
+            if (t + 2 < n_tiles) store_part(kreg, Ks + (t & 1) * KTILE, KL::PITCH);
+            if (t + 1 < n_tiles) store_part(vreg, Vs + ((t + 1) & 1) * VTILE, VL::PITCH);
+            if (t + 3 < n_tiles) load_part(kreg, Kb, p.k_s[2], (t + 3) * BN);
+            if (t + 2 < n_tiles) load_part(vreg, Vb, p.v_s[2], (t + 2) * BN);
+            if (t <= t_last) {
+                // the scores of tile t+1 are computed even when this wave will not
+                // use them (past its last tile): the buffer is in bounds and the
+                // issue slots would otherwise idle
+                scores(s_next, Ks + ((t + 1) & 1) * KTILE);
+                finish_tile(s_cur, t, Vs + (t & 1) * VTILE);
             }
+            __syncthreads();
+        };
+        for (int t = 0; t < n_tiles; t += 2) {
+            iteration(t, sa, sb);
+            if (t + 1 < n_tiles) iteration(t + 1, sb, sa);
+        }
+    } else {
+        f32x16 s[NC];
+        // ---- tile 0 into LDS, tile 1 in flight in registers ----
+        load_part(kreg, Kb, p.k_s[2], 0);
+        load_part(vreg, Vb, p.v_s[2], 0);
+        store_part(kreg, Ks, KL::PITCH);
+        store_part(vreg, Vs, VL::PITCH);
+        if (n_tiles > 1) {
+            load_part(kreg, Kb, p.k_s[2], BN);
+            load_part(vreg, Vb, p.v_s[2], BN);
+        }
+        __syncthreads();
+        for (int t = 0; t < n_tiles; ++t) {
+            if (t <= t_last) {
+                scores(s, Ks + (t & 1) * KTILE);
+                finish_tile(s, t, Vs + (t & 1) * VTILE);
+            }
+            // stage tile t+1 (in registers) into the buffer tile t-1 used, fetch t+2
+            if (t + 1 < n_tiles) {
+                store_part(kreg, Ks + ((t + 1) & 1) * KTILE, KL::PITCH);
+                store_part(vreg, Vs + ((t + 1) & 1) * VTILE, VL::PITCH);
+                if (t + 2 < n_tiles) {
+                    load_part(kreg, Kb, p.k_s[2], (t + 2) * BN);
+                    load_part(vreg, Vb, p.v_s[2], (t + 2) * BN);
+                }
+            }
+            __syncthreads();
         }
     }
-    if (n_tiles > 1) load_part(kreg, Kb, p.k_s[2], BN);
-    load_part(vreg, Vb, p.v_s[2], 0);
-    __syncthreads();
-    if (group_b) __syncthreads();  // group B trails group A by one phase
-
-    for (int t = 0;; ++t) {
-        // ---- matrix phase of tile t: stage K t+1 and V t, P V of t-1, S of t ----
-        if (t + 1 < n_tiles) store_part(kreg, Ks + ((t + 1) & 1) * KTILE, KL::PITCH);
-        if (t < n_tiles) store_part(vreg, Vs + (t & 1) * VTILE, VL::PITCH);
-        if (t + 2 < n_tiles) load_part(kreg, Kb, p.k_s[2], (t + 2) * BN);
-        if (t + 1 < n_tiles) load_part(vreg, Vb, p.v_s[2], (t + 1) * BN);
-        if (t >= 1 && t - 1 <= t_last) pv(Vs + ((t - 1) & 1) * VTILE);
-        if (t < n_tiles && t <= t_last) scores(Ks + (t & 1) * KTILE);
-        if (t == n_tiles) break;
-        __syncthreads();
-        // ---- vector phase of tile t ----
-        if (t <= t_last) vector_phase(t);
-        if (PP) __syncthreads();
-    }
-    if (PP && !group_b) __syncthreads();  // matches group B's extra leading barrier
 
     // ---- epilogue: O = O / l, L = (m + log2 l) ln2 (O = 0, L = 0 if no key) ----
     if (qrow < p.qL) {
@@ -432,18 +448,18 @@ fwd_bf16_kernel(const FwdParams p)
     }
 }
 
-template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, bool PP>
+template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, bool PIPE>
 hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
 {
     const dim3 grid((unsigned)p.n_qtiles * p.Hq * p.B);
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, PP>), grid, dim3(NW * 64), 0, st, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, PIPE>), grid, dim3(NW * 64), 0, st, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
 // Launch shapes per head dimension and mask use: waves per work-group, keys
-// per tile, waves per SIMD, ping-pong.  Eight waves of 32
+// per tile, waves per SIMD, software pipelining.  Eight waves of 32
 // rows share each staged K/V tile where the registers allow two waves per
 // SIMD; at D = 256 the output accumulator alone is 128 registers per lane, so
 // that size runs four waves at one per SIMD.  Overridable at build time for
@@ -467,8 +483,8 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
 #define FA_BF16_D256_MASKED_CFG 4, 32, 1, false
 #endif
 
-#define FA_BF16_VARIANT(D, MASK, CAUSAL, NAME, NW, BN, WPE, PP) \
-    {NAME, 1, D, MASK, CAUSAL, NW * 32, &launch_bf16<D, MASK, CAUSAL, NW, BN, WPE, PP>}
+#define FA_BF16_VARIANT(D, MASK, CAUSAL, NAME, NW, BN, WPE, PIPE) \
+    {NAME, 1, D, MASK, CAUSAL, NW * 32, &launch_bf16<D, MASK, CAUSAL, NW, BN, WPE, PIPE>}
 // expands a CFG macro into separate arguments before FA_BF16_VARIANT sees them
 #define FA_BF16_VARIANT_CFG(...) FA_BF16_VARIANT(__VA_ARGS__)
 

@@ -60,7 +60,7 @@ fwd_f32_kernel(const FwdParams p)
     const int g = lane >> 5;
 
     int id = blockIdx.x;
-    const int h = id % p.Hq;
+    const int h = head_of(id % p.Hq, p.Hq);
     id /= p.Hq;
     const int b = id % p.B;
     id /= p.B;
