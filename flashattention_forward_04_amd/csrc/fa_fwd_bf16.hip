@@ -113,18 +113,10 @@ __device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
 }
 
 // NW waves per work-group (32 query rows each), BN keys per tile, WPE waves
-// per SIMD the register allocation must leave room for, PIPE pipelining.
-//
-// On gfx950 a wave's matrix-core instructions overlap with its own
-// independent vector instructions, but hardly with another wave's on the
-// same SIMD (measured).  With PIPE each wave therefore issues the products
-// for the scores of key tile t+1 in the same instruction stream as the
-// softmax and P V of tile t, so the matrix cores keep running through the
-// softmax.  That puts the K tile one step ahead of the V tile: iteration t
-// reads K tile t+1 and V tile t and stages K tile t+2 and V tile t+1 into
-// the other buffers; the barrier that ends iteration t-1 separates every
-// reuse.  Without PIPE a tile's scores, softmax and P V run back to back.
-template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, bool PIPE>
+// per SIMD the register allocation must leave room for, DIRECT staging of
+// K/V tiles by direct global -> LDS loads (no registers) instead of through
+// registers.
+template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, bool DIRECT>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fwd_bf16_kernel(const FwdParams p)
 {
@@ -132,8 +124,14 @@ fwd_bf16_kernel(const FwdParams p)
     constexpr int BM = NW * 32;
     using KL = TileLayout<D + 8>;     // K tile layout in LDS
     using VL = TileLayout<D + 32>;    // V tile layout in LDS
-    constexpr int KTILE = BN * KL::PITCH;
-    constexpr int VTILE = BN * VL::PITCH;
+    // tiles are padded to whole 1 KiB blocks: one direct load of a wave
+    // fills exactly one block
+    constexpr int KSPR = KL::PITCH / 8;                       // 16-byte slots per K row
+    constexpr int VSPR = VL::PITCH / 8;                       // 16-byte slots per V row
+    constexpr int KINS = (BN * KSPR + 63) / 64;               // 1 KiB blocks per K tile
+    constexpr int VINS = (BN * VSPR + 63) / 64;               // 1 KiB blocks per V tile
+    constexpr int KTILE = KINS * 512;                         // elements per K buffer
+    constexpr int VTILE = VINS * 512;                         // elements per V buffer
     constexpr int DK = D / 16;        // k-steps of S^T over the head dimension
     constexpr int NC = BN / 32;       // 32-key blocks per key tile
     constexpr int ND = D / 32;        // 32-wide blocks of O^T along the head dimension
@@ -141,8 +139,12 @@ fwd_bf16_kernel(const FwdParams p)
     constexpr int SIT = (CH + NT - 1) / NT;  // chunks per thread per tile
     static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * KTILE];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * VTILE];
+    // two buffers each for K and V, as four separate arrays so that the
+    // compiler can tell the buffer being loaded from the one being read
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks0[KTILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks1[KTILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs0[VTILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs1[VTILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -222,6 +224,37 @@ fwd_bf16_kernel(const FwdParams p)
             if (CH % NT == 0 || c < CH) *(u32x4*)(lds + (c / (D / 8)) * pitch + (c % (D / 8)) * 8) = r[it];
         }
     };
+
+    // Direct global -> LDS staging: 1 KiB block i of a tile is filled by one
+    // global_load_lds_dwordx4 of wave i % NW, whose lane l writes slot 64i + l
+    // (the hardware places lane l's 16 bytes at the block base + 16 l).  A
+    // slot in a row's pad is skipped; rows past kL load row kL - 1 (finite
+    // values; their scores are masked, so they only meet P = 0).
+    auto issue_tile = [&](const uint16_t* gbase, int64_t stride, int j0, uint16_t* lds, auto spr_c, auto nins_c)
+        __attribute__((always_inline)) {
+        constexpr int SPR = decltype(spr_c)::value;
+        constexpr int NINS = decltype(nins_c)::value;
+#pragma unroll
+        for (int k = 0; k < (NINS + NW - 1) / NW; ++k) {
+            const int i = wave + k * NW;
+            if (NINS % NW != 0 && i >= NINS) break;
+            const int slot = 64 * i + lane;
+            const int row = slot / SPR;
+            const int ch = slot % SPR;
+            if (ch < D / 8 && row < BN) {
+                const int j = min(j0 + row, p.kL - 1);
+                __builtin_amdgcn_global_load_lds(
+                    (__attribute__((address_space(1))) void*)(gbase + (int64_t)j * stride + ch * 8),
+                    (__attribute__((address_space(3))) void*)(lds + 512 * i), 16, 0, 0);
+            }
+        }
+    };
+    auto issue_kv = [&](int t, uint16_t* kt, uint16_t* vt) __attribute__((always_inline)) {
+        issue_tile(Kb, p.k_s[2], t * BN, kt, std::integral_constant<int, KSPR>{}, std::integral_constant<int, KINS>{});
+        issue_tile(Vb, p.v_s[2], t * BN, vt, std::integral_constant<int, VSPR>{}, std::integral_constant<int, VINS>{});
+    };
+    // all of this wave's direct loads have landed in LDS
+    auto wait_loads = []() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
     // ---- S^T = K Q^T for the key tile staged at kt ----
     auto scores = [&](f32x16 (&s)[NC], const uint16_t* kt) __attribute__((always_inline)) {
@@ -362,49 +395,33 @@ fwd_bf16_kernel(const FwdParams p)
         }
     };
 
-    u32x4 kreg[SIT], vreg[SIT];
-    if (PIPE) {
-        f32x16 sa[NC], sb[NC];
-        // ---- prologue: K tiles 0, 1 and V tile 0 in LDS; scores of tile 0 ----
-        load_part(kreg, Kb, p.k_s[2], 0);
-        load_part(vreg, Vb, p.v_s[2], 0);
-        store_part(kreg, Ks, KL::PITCH);
-        store_part(vreg, Vs, VL::PITCH);
-        load_part(kreg, Kb, p.k_s[2], BN);
-        store_part(kreg, Ks + KTILE, KL::PITCH);
-        __syncthreads();
-        if (t_last >= 0) scores(sa, Ks);
-        load_part(kreg, Kb, p.k_s[2], 2 * BN);
-        load_part(vreg, Vb, p.v_s[2], BN);
-        __syncthreads();  // K tile 0's buffer is restaged in iteration 0
-
-        // iteration t: stage K t+2 and V t+1, scores of t+1 into s_next, and
-        // softmax + P V of tile t from s_cur
-        auto iteration = [&](int t, f32x16 (&s_cur)[NC], f32x16 (&s_next)[NC]) __attribute__((always_inline)) {
-            if (t + 2 < n_tiles) store_part(kreg, Ks + (t & 1) * KTILE, KL::PITCH);
-            if (t + 1 < n_tiles) store_part(vreg, Vs + ((t + 1) & 1) * VTILE, VL::PITCH);
-            if (t + 3 < n_tiles) load_part(kreg, Kb, p.k_s[2], (t + 3) * BN);
-            if (t + 2 < n_tiles) load_part(vreg, Vb, p.v_s[2], (t + 2) * BN);
+    f32x16 s[NC];
+    if (DIRECT) {
+        // tile t+1 is loaded straight into LDS while tile t is computed; the
+        // loop is unrolled by two so every buffer choice is static
+        auto step = [&](int t, uint16_t* kc, uint16_t* vc, uint16_t* kn, uint16_t* vn) __attribute__((always_inline)) {
+            if (t + 1 < n_tiles) issue_kv(t + 1, kn, vn);  // into the buffers tile t-1 used
             if (t <= t_last) {
-                // the scores of tile t+1 are computed even when this wave will not
-                // use them (past its last tile): the buffer is in bounds and the
-                // issue slots would otherwise idle
-                scores(s_next, Ks + ((t + 1) & 1) * KTILE);
-                finish_tile(s_cur, t, Vs + (t & 1) * VTILE);
+                scores(s, kc);
+                finish_tile(s, t, vc);
             }
+            wait_loads();
             __syncthreads();
         };
+        issue_kv(0, Ks0, Vs0);
+        wait_loads();
+        __syncthreads();
         for (int t = 0; t < n_tiles; t += 2) {
-            iteration(t, sa, sb);
-            if (t + 1 < n_tiles) iteration(t + 1, sb, sa);
+            step(t, Ks0, Vs0, Ks1, Vs1);
+            if (t + 1 < n_tiles) step(t + 1, Ks1, Vs1, Ks0, Vs0);
         }
     } else {
-        f32x16 s[NC];
+        u32x4 kreg[SIT], vreg[SIT];
         // ---- tile 0 into LDS, tile 1 in flight in registers ----
         load_part(kreg, Kb, p.k_s[2], 0);
         load_part(vreg, Vb, p.v_s[2], 0);
-        store_part(kreg, Ks, KL::PITCH);
-        store_part(vreg, Vs, VL::PITCH);
+        store_part(kreg, Ks0, KL::PITCH);
+        store_part(vreg, Vs0, VL::PITCH);
         if (n_tiles > 1) {
             load_part(kreg, Kb, p.k_s[2], BN);
             load_part(vreg, Vb, p.v_s[2], BN);
@@ -412,13 +429,13 @@ fwd_bf16_kernel(const FwdParams p)
         __syncthreads();
         for (int t = 0; t < n_tiles; ++t) {
             if (t <= t_last) {
-                scores(s, Ks + (t & 1) * KTILE);
-                finish_tile(s, t, Vs + (t & 1) * VTILE);
+                scores(s, (t & 1) ? Ks1 : Ks0);
+                finish_tile(s, t, (t & 1) ? Vs1 : Vs0);
             }
             // stage tile t+1 (in registers) into the buffer tile t-1 used, fetch t+2
             if (t + 1 < n_tiles) {
-                store_part(kreg, Ks + ((t + 1) & 1) * KTILE, KL::PITCH);
-                store_part(vreg, Vs + ((t + 1) & 1) * VTILE, VL::PITCH);
+                store_part(kreg, (t & 1) ? Ks0 : Ks1, KL::PITCH);
+                store_part(vreg, (t & 1) ? Vs0 : Vs1, VL::PITCH);
                 if (t + 2 < n_tiles) {
                     load_part(kreg, Kb, p.k_s[2], (t + 2) * BN);
                     load_part(vreg, Vb, p.v_s[2], (t + 2) * BN);
@@ -448,18 +465,18 @@ fwd_bf16_kernel(const FwdParams p)
     }
 }
 
-template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, bool PIPE>
+template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, bool DIRECT>
 hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
 {
     const dim3 grid((unsigned)p.n_qtiles * p.Hq * p.B);
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, PIPE>), grid, dim3(NW * 64), 0, st, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, DIRECT>), grid, dim3(NW * 64), 0, st, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
 // Launch shapes per head dimension and mask use: waves per work-group, keys
-// per tile, waves per SIMD, software pipelining.  Eight waves of 32
+// per tile, waves per SIMD, direct global -> LDS staging.  Eight waves of 32
 // rows share each staged K/V tile where the registers allow two waves per
 // SIMD; at D = 256 the output accumulator alone is 128 registers per lane, so
 // that size runs four waves at one per SIMD.  Overridable at build time for
@@ -471,7 +488,7 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
 #define FA_BF16_D64_MASKED_CFG 4, 64, 2, false
 #endif
 #ifndef FA_BF16_D128_CFG
-#define FA_BF16_D128_CFG 8, 64, 2, false
+#define FA_BF16_D128_CFG 8, 64, 2, true
 #endif
 #ifndef FA_BF16_D128_MASKED_CFG
 #define FA_BF16_D128_MASKED_CFG 8, 64, 2, false
@@ -483,8 +500,8 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
 #define FA_BF16_D256_MASKED_CFG 4, 32, 1, false
 #endif
 
-#define FA_BF16_VARIANT(D, MASK, CAUSAL, NAME, NW, BN, WPE, PIPE) \
-    {NAME, 1, D, MASK, CAUSAL, NW * 32, &launch_bf16<D, MASK, CAUSAL, NW, BN, WPE, PIPE>}
+#define FA_BF16_VARIANT(D, MASK, CAUSAL, NAME, NW, BN, WPE, DIRECT) \
+    {NAME, 1, D, MASK, CAUSAL, NW * 32, &launch_bf16<D, MASK, CAUSAL, NW, BN, WPE, DIRECT>}
 // expands a CFG macro into separate arguments before FA_BF16_VARIANT sees them
 #define FA_BF16_VARIANT_CFG(...) FA_BF16_VARIANT(__VA_ARGS__)
 
