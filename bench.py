@@ -233,8 +233,11 @@ def cpu_baseline(w, q, k, v, mask, target_s: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the default warm-up (about 50 ms of work) lets the clocks settle after
+    # the power dip that follows the first launches of a busy kernel, so the
+    # timed steps measure the sustained rate
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="causal_bf16_d128_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

@@ -23,6 +23,12 @@ ARCH = "gfx950"
 
 SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_fwd_f32.hip"]
 
+# Per-source code generation options.  The bf16 kernels keep every matrix
+# accumulator in ordinary VGPRs: their softmax works on the score
+# accumulators with vector instructions, and for D = 256 the default (AGPR)
+# form makes the register allocator shuffle accumulators and spill.
+SOURCE_FLAGS = {"fa_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -41,7 +47,7 @@ def _flags():
 def _compile(src: str, extra=()) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc(), *_flags(), *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *_flags(), *SOURCE_FLAGS.get(src, []), *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile of {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

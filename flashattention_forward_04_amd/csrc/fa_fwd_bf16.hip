@@ -29,17 +29,23 @@
 //     permutation of a 16-key chunk, and the V^T operand is read in that same
 //     key order with two gfx950 transposing LDS reads (ds_read_b64_tr_b16),
 //     so V is staged exactly like K: no VALU transposition.
-//   * K and V are staged in LDS row-major with a padded pitch and an XOR
-//     swizzle of 16-byte chunks (TileLayout) that measures conflict-free on
-//     gfx950 for every access the kernel makes.  Tiles are double-buffered:
-//     tile t+1 is loaded into registers while tile t is computed, so one
-//     barrier per tile suffices and global latency is hidden.
+//   * K and V are staged in LDS row-major with padded row pitches that
+//     measure conflict-free on gfx950 for every access the kernel makes
+//     (TileLayout).  Tiles go straight from global memory into LDS
+//     (global_load_lds_dwordx4, no registers) round a ring of LDS buffers,
+//     loaded one or more tiles ahead, with one barrier per tile.
+//   * Two instruction schedules: plain (score products of tile t, then its
+//     softmax with the P V products interleaved block by block) and
+//     pipelined (the score products of tile t+1 are spread through the
+//     softmax of tile t, so a wave always has matrix work beside its vector
+//     work).  Which one each head dimension uses was chosen by timing.
 //   * Causal work-groups are issued longest-first, and key tiles past the
 //     last query row of a work-group are never loaded (forge
 //     flash_attention_mma.metal, the causal j_end bound); a wave whose rows
 //     all precede a key tile skips that tile's arithmetic.
 //   * Ragged tails: query rows past qL load zeros and are not stored; key
-//     rows past kL are staged as zeros and their scores masked to -inf.
+//     rows past kL repeat row kL - 1 (finite values) and their scores are
+//     masked to -inf.
 #include "fa_common.h"
 
 #include <math.h>
@@ -89,6 +95,17 @@ __device__ __forceinline__ float row_sum_halves(float x) {
 // on almost every tile.
 constexpr float kRescaleSlack = 8.f;
 
+// Vector instructions placed after each matrix product in the softmax
+// stages (chosen by timing on MI355X).
+#ifndef FA_SCHED_PV
+#define FA_SCHED_PV 4
+#endif
+// K operand reads kept in flight ahead of the score products of a whole
+// tile (0 = leave it to the compiler).
+#ifndef FA_SCHED_S
+#define FA_SCHED_S 4
+#endif
+
 // K and V tiles live in LDS row-major ([BN][D], one key per row) with a
 // padded row pitch: D + 8 elements for K, D + 32 for V.  Measured on gfx950
 // (for D = 64, 128 and 256) these pitches have no bank conflicts for the
@@ -101,6 +118,28 @@ struct TileLayout {
     __device__ static __forceinline__ int off(int row, int chunk) { return row * P + chunk * 8; }
 };
 
+// One direct global -> LDS load (global_load_lds_dwordx4): lane l's 16
+// bytes land at LDS byte address lds_base + 16 l.  It is issued from inline
+// assembly so that the compiler does not track it: while a direct load it
+// knows of is in flight, the compiler turns every wait for an LDS read into
+// a wait for all of them, which serialises the operand reads with the
+// matrix products.  Completion is ordered instead by the key loop's explicit
+// vmcnt waits and barriers (a load the compiler does not know of can only
+// make its own waits wait longer).  M0 is saved and restored around it.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0"
+        : "=&s"(saved)
+        : "v"(gsrc), "s"(lds_base)
+        : "memory");
+}
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -112,39 +151,67 @@ __device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
 }
 
-// NW waves per work-group (32 query rows each), BN keys per tile, WPE waves
-// per SIMD the register allocation must leave room for, DIRECT staging of
-// K/V tiles by direct global -> LDS loads (no registers) instead of through
-// registers.
-template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, bool DIRECT>
+// One work-group: NW waves of 32 query rows each, BN keys per tile, WPE
+// waves per SIMD the register allocation must leave room for.
+//
+// PIPE (software pipelining across key tiles): the score products of tile
+// t+1 are issued in between the softmax instructions of tile t.  A wave's
+// vector instructions run while its own matrix products execute, but hardly
+// while another wave's do, so a wave that interleaves both kinds of work
+// keeps the matrix cores busy through the softmax.  K is then staged one
+// tile ahead of V.
+//
+// K/V tiles are loaded straight from global memory into LDS (no registers),
+// double-buffered, with one barrier per tile.
+template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fwd_bf16_kernel(const FwdParams p)
 {
-    constexpr int NT = NW * 64;
-    constexpr int BM = NW * 32;
+    constexpr bool PIPE = SCHED != 0;  // next tile's scores formed during this tile's softmax
+    constexpr int BM = NW * 32;       // query rows per work-group
     using KL = TileLayout<D + 8>;     // K tile layout in LDS
     using VL = TileLayout<D + 32>;    // V tile layout in LDS
     // tiles are padded to whole 1 KiB blocks: one direct load of a wave
     // fills exactly one block
-    constexpr int KSPR = KL::PITCH / 8;                       // 16-byte slots per K row
-    constexpr int VSPR = VL::PITCH / 8;                       // 16-byte slots per V row
-    constexpr int KINS = (BN * KSPR + 63) / 64;               // 1 KiB blocks per K tile
-    constexpr int VINS = (BN * VSPR + 63) / 64;               // 1 KiB blocks per V tile
-    constexpr int KTILE = KINS * 512;                         // elements per K buffer
-    constexpr int VTILE = VINS * 512;                         // elements per V buffer
-    constexpr int DK = D / 16;        // k-steps of S^T over the head dimension
-    constexpr int NC = BN / 32;       // 32-key blocks per key tile
-    constexpr int ND = D / 32;        // 32-wide blocks of O^T along the head dimension
-    constexpr int CH = BN * D / 8;    // 16-byte chunks per tile
-    constexpr int SIT = (CH + NT - 1) / NT;  // chunks per thread per tile
+    constexpr int KSPR = KL::PITCH / 8;          // 16-byte slots per K row
+    constexpr int VSPR = VL::PITCH / 8;          // 16-byte slots per V row
+    constexpr int KINS = (BN * KSPR + 63) / 64;  // 1 KiB blocks per K tile
+    constexpr int VINS = (BN * VSPR + 63) / 64;  // 1 KiB blocks per V tile
+    constexpr int KTILE = KINS * 512;            // elements per K buffer
+    constexpr int VTILE = VINS * 512;            // elements per V buffer
+    constexpr int DK = D / 16;                   // k-steps of S^T over the head dimension
+    constexpr int NC = BN / 32;                  // 32-key blocks per key tile
+    constexpr int ND = D / 32;                   // 32-wide blocks of O^T along the head dimension
+    constexpr int NP = DK * NC;                  // score products per tile
     static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
 
-    // two buffers each for K and V, as four separate arrays so that the
-    // compiler can tell the buffer being loaded from the one being read
+    // NB buffers each for K and V, as separate arrays so that the compiler
+    // can tell the buffer being loaded from the ones being read
+    static_assert(NB == 2 || NB == 4, "ring depth");
+    constexpr int KT2 = NB > 2 ? KTILE : 1, VT2 = NB > 2 ? VTILE : 1;
     __shared__ __attribute__((aligned(1024))) uint16_t Ks0[KTILE];
     __shared__ __attribute__((aligned(1024))) uint16_t Ks1[KTILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks2[KT2];
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks3[KT2];
     __shared__ __attribute__((aligned(1024))) uint16_t Vs0[VTILE];
     __shared__ __attribute__((aligned(1024))) uint16_t Vs1[VTILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs2[VT2];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs3[VT2];
+    auto kbuf = [&](auto i_c) __attribute__((always_inline)) -> uint16_t* {
+        constexpr int I = decltype(i_c)::value;
+        return I == 0 ? Ks0 : I == 1 ? Ks1 : I == 2 ? Ks2 : Ks3;
+    };
+    auto vbuf = [&](auto i_c) __attribute__((always_inline)) -> uint16_t* {
+        constexpr int I = decltype(i_c)::value;
+        return I == 0 ? Vs0 : I == 1 ? Vs1 : I == 2 ? Vs2 : Vs3;
+    };
+    // the same by a (fully unrolled, hence constant) index
+    auto kbuf_dyn = [&](int i) __attribute__((always_inline)) -> uint16_t* {
+        return i == 0 ? Ks0 : i == 1 ? Ks1 : i == 2 ? Ks2 : Ks3;
+    };
+    auto vbuf_dyn = [&](int i) __attribute__((always_inline)) -> uint16_t* {
+        return i == 0 ? Vs0 : i == 1 ? Vs1 : i == 2 ? Vs2 : Vs3;
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -164,13 +231,13 @@ fwd_bf16_kernel(const FwdParams p)
     const int q0 = qt * BM;
     const int hk = h / p.group;
     const int wq0 = q0 + wave * 32;  // first query row of this wave
-    const int qrow = wq0 + r32;
+    const int qrow = wq0 + r32;      // this lane's query row
 
     const uint16_t* Qb = (const uint16_t*)p.q + b * p.q_s[0] + h * p.q_s[1];
     const uint16_t* Kb = (const uint16_t*)p.k + b * p.k_s[0] + hk * p.k_s[1];
     const uint16_t* Vb = (const uint16_t*)p.v + b * p.v_s[0] + hk * p.v_s[1];
 
-    // ---- Q fragments: row qrow, elements 16ks + 8g .. +7 ----
+    // ---- Q fragments: row qrow, elements 16ks + 8g .. +7 (zeros past qL) ----
     bf16x8 qf[DK];
     {
         const bool in = qrow < p.qL;
@@ -206,25 +273,6 @@ fwd_bf16_kernel(const FwdParams p)
     float m_run = -INFINITY;  // running max (base 2) that P is taken against
     float l_run = 0.f;        // running sum of P
 
-    // ---- staging: this thread's chunks of a tile, global -> registers -> LDS ----
-    auto load_part = [&](u32x4 (&r)[SIT], const uint16_t* base, int64_t stride, int j0) __attribute__((always_inline)) {
-#pragma unroll
-        for (int it = 0; it < SIT; ++it) {
-            const int c = tid + it * NT;
-            const int j = j0 + c / (D / 8);
-            r[it] = u32x4{0, 0, 0, 0};  // keys past kL stay zero: 0 * garbage never reaches O
-            if ((CH % NT == 0 || c < CH) && j < p.kL)
-                r[it] = *(const u32x4*)(base + (int64_t)j * stride + (c % (D / 8)) * 8);
-        }
-    };
-    auto store_part = [&](const u32x4 (&r)[SIT], uint16_t* lds, int pitch) __attribute__((always_inline)) {
-#pragma unroll
-        for (int it = 0; it < SIT; ++it) {
-            const int c = tid + it * NT;
-            if (CH % NT == 0 || c < CH) *(u32x4*)(lds + (c / (D / 8)) * pitch + (c % (D / 8)) * 8) = r[it];
-        }
-    };
-
     // Direct global -> LDS staging: 1 KiB block i of a tile is filled by one
     // global_load_lds_dwordx4 of wave i % NW, whose lane l writes slot 64i + l
     // (the hardware places lane l's 16 bytes at the block base + 16 l).  A
@@ -243,31 +291,52 @@ fwd_bf16_kernel(const FwdParams p)
             const int ch = slot % SPR;
             if (ch < D / 8 && row < BN) {
                 const int j = min(j0 + row, p.kL - 1);
-                __builtin_amdgcn_global_load_lds(
-                    (__attribute__((address_space(1))) void*)(gbase + (int64_t)j * stride + ch * 8),
-                    (__attribute__((address_space(3))) void*)(lds + 512 * i), 16, 0, 0);
+                if (MASK == MASK_NONE) {
+                    lds_dma16(gbase + (int64_t)j * stride + ch * 8,
+                              (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(lds + 512 * i));
+                } else {
+                    // the masked kernels load the mask with ordinary loads
+                    // whose compiler waits would also wait for untracked
+                    // direct loads, so here the compiler tracks them
+                    __builtin_amdgcn_global_load_lds(
+                        (__attribute__((address_space(1))) void*)(gbase + (int64_t)j * stride + ch * 8),
+                        (__attribute__((address_space(3))) void*)(lds + 512 * i), 16, 0, 0);
+                }
             }
         }
     };
-    auto issue_kv = [&](int t, uint16_t* kt, uint16_t* vt) __attribute__((always_inline)) {
+    auto issue_k = [&](int t, uint16_t* kt) __attribute__((always_inline)) {
         issue_tile(Kb, p.k_s[2], t * BN, kt, std::integral_constant<int, KSPR>{}, std::integral_constant<int, KINS>{});
+    };
+    auto issue_v = [&](int t, uint16_t* vt) __attribute__((always_inline)) {
         issue_tile(Vb, p.v_s[2], t * BN, vt, std::integral_constant<int, VSPR>{}, std::integral_constant<int, VINS>{});
     };
     // all of this wave's direct loads have landed in LDS
     auto wait_loads = []() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
-    // ---- S^T = K Q^T for the key tile staged at kt ----
-    auto scores = [&](f32x16 (&s)[NC], const uint16_t* kt) __attribute__((always_inline)) {
+    // ---- S^T = K Q^T for the key tile staged at kt: products [i0, i1) of
+    // the NP, in k-step-major order (consecutive products feed different
+    // accumulators) ----
+    auto score_products = [&](f32x16 (&s)[NC], const uint16_t* kt, int i0, int i1) __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < NC; ++c) s[c] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < DK; ++ks) {
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const bf16x8 kop = *(const bf16x8*)(kt + KL::off(32 * c + r32, 2 * ks + g));
-                s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[ks], s[c], 0, 0, 0);
-            }
+        for (int i = 0; i < NP; ++i) {
+            if (i < i0 || i >= i1) continue;
+            const int ks = i / NC, c = i % NC;
+            const bf16x8 kop = *(const bf16x8*)(kt + KL::off(32 * c + r32, 2 * ks + g));
+            s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[ks], ks == 0 ? f32x16{} : s[c], 0, 0, 0);
         }
+#if FA_SCHED_S
+        // keep FA_SCHED_S operand reads in flight ahead of the products
+        if (i0 == 0 && i1 == NP) {
+            __builtin_amdgcn_sched_group_barrier(0x100, FA_SCHED_S, 3);
+#pragma unroll
+            for (int i = 0; i < NP - FA_SCHED_S; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, FA_SCHED_S, 3);
+        }
+#endif
     };
 
     // ---- scores of key tile j0 -> base 2, excluded keys at -inf: keys past
@@ -328,14 +397,121 @@ fwd_bf16_kernel(const FwdParams p)
     };
 
     // ---- online softmax of s (raw when cs == c2, base 2 when cs == 1), then
-    // O^T += V^T P^T from the value tile staged at vt ----
-    auto softmax_pv = [&](f32x16 (&s)[NC], float cs, const uint16_t* vt) __attribute__((always_inline)) {
+    // O^T += V^T P^T from the value tile staged at vt; in pipelined mode the
+    // next tile's score products (into sn, from the K tile staged at kn) are
+    // interleaved.
+    //
+    // The work is laid out as a static software pipeline so that every
+    // matrix product has vector work beside it and every LDS operand is read
+    // one stage before it is used:
+    //   stage -1: row max and rescale decision; score products of group 0
+    //   stage r (0 .. NCH): P V of 16-key block r-1, score products of
+    //             group r+1, P of block r; reads V^T operands of block r and
+    //             K operands of group r+2.
+    // Stages are fenced (sched_barrier), and inside a stage the products and
+    // vector instructions are issued alternately (sched_group_barrier).
+    //
+    // ORD says where the next tile's score products go: 0 nowhere (not
+    // pipelined), 1 spread over the stages as above, 2 all in stage -1, 3 all
+    // after the last P V.  Orders 2 and 3 run on the two halves of the waves
+    // (ping-pong): the two waves sharing a SIMD then issue their products at
+    // different times, and one wave's vector work runs beside the other's
+    // products.
+    auto softmax_pv = [&](f32x16 (&s)[NC], float cs, const uint16_t* vt, f32x16 (&sn)[NC], const uint16_t* kn,
+                          auto ord_c) __attribute__((always_inline)) {
+        constexpr int ORD = decltype(ord_c)::value;
+        constexpr int NCH = 2 * NC;                                // 16-key blocks per tile
+        constexpr int NS = (ORD == 1) ? NP : 0;                    // products spread over the stages
+        constexpr int SS = (ORD == 1) ? (NP + NCH) / (NCH + 1) : 0;  // products per group
+        constexpr int SSB = SS > 0 ? SS : 1;
+        bf16x8 kb[2][SSB];  // K operands, by group parity
+        bf16x8 vb[2][ND];   // V^T operands, by block parity
+        bf16x8 pf[2];       // P operands, by block parity
+        const int lt = lane & 15;
+
+        auto k_read = [&](int grp) __attribute__((always_inline)) {
+#pragma unroll
+            for (int jj = 0; jj < SS; ++jj) {
+                const int i = grp * SS + jj;
+                if (i < NS) kb[grp & 1][jj] = *(const bf16x8*)(kn + KL::off(32 * (i % NC) + r32, 2 * (i / NC) + g));
+            }
+        };
+        auto s_mma = [&](int grp) __attribute__((always_inline)) {
+#pragma unroll
+            for (int jj = 0; jj < SS; ++jj) {
+                const int i = grp * SS + jj;
+                if (i < NS) {
+                    const int ks = i / NC, c = i % NC;
+                    sn[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[grp & 1][jj], qf[ks], ks == 0 ? f32x16{} : sn[c],
+                                                                     0, 0, 0);
+                }
+            }
+        };
+        auto v_read = [&](int kidx) __attribute__((always_inline)) {
+#pragma unroll
+            for (int d = 0; d < ND; ++d) {
+                // lane l: head-dim column 32d + l%32, keys 16kidx + 4g + {0..3}
+                // and 16kidx + 8 + 4g + {0..3}, the order P is packed in
+                const int col = 32 * d + 16 * ((lane >> 4) & 1) + 4 * (lt & 3);
+                const int row0 = 16 * kidx + 4 * g + (lt >> 2);
+                const i16x4 v0 = lds_read_tr(vt + VL::off(row0, 0) + col);
+                const i16x4 v1 = lds_read_tr(vt + VL::off(row0 + 8, 0) + col);
+                vb[kidx & 1][d] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        };
+        auto pv_mma = [&](int kidx) __attribute__((always_inline)) {
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[kidx & 1][d], pf[kidx & 1], o[d], 0, 0, 0);
+        };
+
+        // all NP score products of the next tile, reading their K operands as
+        // they go (orders 2 and 3)
+        auto s_block = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const int ks = i / NC, c = i % NC;
+                const bf16x8 kop = *(const bf16x8*)(kn + KL::off(32 * c + r32, 2 * ks + g));
+                sn[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[ks], ks == 0 ? f32x16{} : sn[c], 0, 0, 0);
+            }
+            // keep four operand reads in flight ahead of the products
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
+#pragma unroll
+            for (int i = 0; i < NP - 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 2);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 2);
+        };
+
+        if (ORD == 2) {
+            s_block();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // stage -1: group 0's operands are needed at once (their latency is
+        // covered by the row max); group 1's are read behind the first product
+        k_read(0);
         float mx = s[0][0];
 #pragma unroll
         for (int c = 0; c < NC; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c][r]);
         const float m_tile = row_max_halves(mx) * cs;
+        s_mma(0);
+        k_read(1);
+        if (ORD == 1) {
+            __builtin_amdgcn_sched_group_barrier(0x100, SS, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, SS, 0);
+#pragma unroll
+            for (int i = 1; i < SS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
         if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
             const float m_new = fmaxf(m_run, m_tile);
             if (m_run != -INFINITY && m_new != m_run) {
@@ -350,11 +526,14 @@ fwd_bf16_kernel(const FwdParams p)
         // the row sum is taken in fp32 before P is rounded to bf16: L must
         // stay within 1e-3 even for rows that see only a few keys
         float rs0 = 0.f, rs1 = 0.f;
-        const int lt = lane & 15;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
+        for (int r = 0; r <= NCH; ++r) {
+            if (r < NCH) v_read(r);
+            if (r + 2 <= NCH) k_read(r + 2);
+            if (r >= 1) pv_mma(r - 1);
+            if (r + 1 <= NCH) s_mma(r + 1);
+            if (r < NCH) {
+                const int c = r >> 1, hh = r & 1;
                 u32x4 pw;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -364,84 +543,114 @@ fwd_bf16_kernel(const FwdParams p)
                     rs0 += a;
                     rs1 += z;
                 }
-                const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-                const int kidx = 2 * c + hh;
-#pragma unroll
-                for (int d = 0; d < ND; ++d) {
-                    // lane l: head-dim column 32d + l%32, keys 16kidx + 4g + {0..3}
-                    // and 16kidx + 8 + 4g + {0..3}, the order P was packed in
-                    const int col = 32 * d + 16 * ((lane >> 4) & 1) + 4 * (lt & 3);
-                    const int row0 = 16 * kidx + 4 * g + (lt >> 2);
-                    const i16x4 v0 = lds_read_tr(vt + VL::off(row0, 0) + col);
-                    const i16x4 v1 = lds_read_tr(vt + VL::off(row0 + 8, 0) + col);
-                    const bf16x8 vop =
-                        __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-                    o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pf, o[d], 0, 0, 0);
-                }
+                pf[r & 1] = __builtin_bit_cast(bf16x8, pw);
             }
+            // one product first (its wait retires the previous stage's
+            // reads, so no more than one stage of reads is ever in flight),
+            // then this stage's reads, then products and vector work
+            // alternately
+            constexpr int kMfma = ND + SS;
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * ND + SS, 1);
+#pragma unroll
+            for (int i = 1; i < kMfma; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x002, FA_SCHED_PV, 1);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (ORD == 3) {
+            s_block();
+            __builtin_amdgcn_sched_barrier(0);
         }
         l_run += row_sum_halves(rs0 + rs1);
     };
 
     // softmax and P V of tile t with its scores in s
-    auto finish_tile = [&](f32x16 (&s)[NC], int t, const uint16_t* vt) __attribute__((always_inline)) {
+    auto finish_tile = [&](int t, f32x16 (&s)[NC], const uint16_t* vt, f32x16 (&sn)[NC], const uint16_t* kn)
+        __attribute__((always_inline)) {
         const int j0 = t * BN;
         const bool masked = (MASK != MASK_NONE) || (j0 + BN > p.kL) || (CAUSAL && j0 + BN - 1 > wq0);
-        if (masked) {
-            apply_mask(s, j0);
-            softmax_pv(s, 1.f, vt);
+        // one softmax for both kinds of tile, so that the accumulators and
+        // the next tile's scores are written in one place (two copies of the
+        // softmax would make the register allocator move them at the join)
+        if (masked) apply_mask(s, j0);
+        const float cs = masked ? 1.f : c2;
+        if (SCHED == 0) {
+            softmax_pv(s, cs, vt, sn, kn, std::integral_constant<int, 0>{});
+        } else if (SCHED == 1) {
+            softmax_pv(s, cs, vt, sn, kn, std::integral_constant<int, 1>{});
+        } else if (2 * wave < NW) {
+            softmax_pv(s, cs, vt, sn, kn, std::integral_constant<int, 2>{});
         } else {
-            softmax_pv(s, c2, vt);
+            softmax_pv(s, cs, vt, sn, kn, std::integral_constant<int, 3>{});
         }
     };
 
-    f32x16 s[NC];
-    if (DIRECT) {
-        // tile t+1 is loaded straight into LDS while tile t is computed; the
-        // loop is unrolled by two so every buffer choice is static
-        auto step = [&](int t, uint16_t* kc, uint16_t* vc, uint16_t* kn, uint16_t* vn) __attribute__((always_inline)) {
-            if (t + 1 < n_tiles) issue_kv(t + 1, kn, vn);  // into the buffers tile t-1 used
-            if (t <= t_last) {
-                scores(s, kc);
-                finish_tile(s, t, vc);
-            }
+    f32x16 sa[NC], sb[NC];  // score tiles (two, for the pipelined schedule)
+
+    // ---- the key loop.  K and V tiles go round rings of NB LDS buffers
+    // (tile t in buffer t % NB); step t loads K of tile t + PK and V of tile
+    // t + PV, each into the buffer that was last read in step t - 1, so one
+    // barrier per step covers every reuse.  The loop is unrolled by NB so
+    // every buffer choice is static.
+    constexpr int PK = PIPE ? NB : NB - 1;  // load-ahead distance of K
+    constexpr int PV = NB - 1;              // load-ahead distance of V
+    // loads this wave issues per tile (the fewest any wave issues)
+    constexpr int kLoadsPerStep = KINS / NW + VINS / NW;
+    // At the end of step t, what step t+1 reads was issued at step t+2-NB or
+    // earlier, so the loads of the last NB-2 steps may stay in flight (when
+    // all of them were issued; near the end everything is waited for).
+    constexpr int kPending = (NB - 2) * kLoadsPerStep;
+    static_assert(kPending < 64, "vmcnt range");
+    auto end_step = [&](int t) __attribute__((always_inline)) {
+        if (kPending > 0 && t + PK < n_tiles)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (kPending & 15) | ((kPending >> 4) << 14));
+        else
             wait_loads();
-            __syncthreads();
-        };
-        issue_kv(0, Ks0, Vs0);
-        wait_loads();
         __syncthreads();
-        for (int t = 0; t < n_tiles; t += 2) {
-            step(t, Ks0, Vs0, Ks1, Vs1);
-            if (t + 1 < n_tiles) step(t + 1, Ks1, Vs1, Ks0, Vs0);
-        }
-    } else {
-        u32x4 kreg[SIT], vreg[SIT];
-        // ---- tile 0 into LDS, tile 1 in flight in registers ----
-        load_part(kreg, Kb, p.k_s[2], 0);
-        load_part(vreg, Vb, p.v_s[2], 0);
-        store_part(kreg, Ks0, KL::PITCH);
-        store_part(vreg, Vs0, VL::PITCH);
-        if (n_tiles > 1) {
-            load_part(kreg, Kb, p.k_s[2], BN);
-            load_part(vreg, Vb, p.v_s[2], BN);
-        }
-        __syncthreads();
-        for (int t = 0; t < n_tiles; ++t) {
-            if (t <= t_last) {
-                scores(s, (t & 1) ? Ks1 : Ks0);
-                finish_tile(s, t, (t & 1) ? Vs1 : Vs0);
+    };
+    auto step = [&](int t, auto u_c) __attribute__((always_inline)) {
+        constexpr int U = decltype(u_c)::value;  // t % NB
+        f32x16(&sc)[NC] = (U & 1) ? sb : sa;
+        f32x16(&sn)[NC] = (U & 1) ? sa : sb;
+        if (t + PK < n_tiles) issue_k(t + PK, kbuf(std::integral_constant<int, (U + PK) % NB>{}));
+        if (t + PV < n_tiles) issue_v(t + PV, vbuf(std::integral_constant<int, (U + PV) % NB>{}));
+        if (t <= t_last) {
+            const uint16_t* vr = vbuf(std::integral_constant<int, U>{});
+            if (PIPE) {
+                // the next tile's scores are formed even past t_last (from
+                // whatever its K buffer holds): keeping them unconditional
+                // keeps them in the same instruction stream as this softmax,
+                // and a result that is not needed is never read
+                finish_tile(t, sc, vr, sn, kbuf(std::integral_constant<int, (U + 1) % NB>{}));
+            } else {
+                const uint16_t* kr = kbuf(std::integral_constant<int, U>{});
+                score_products(sa, kr, 0, NP);
+                finish_tile(t, sa, vr, sb, kr);
             }
-            // stage tile t+1 (in registers) into the buffer tile t-1 used, fetch t+2
-            if (t + 1 < n_tiles) {
-                store_part(kreg, (t & 1) ? Ks0 : Ks1, KL::PITCH);
-                store_part(vreg, (t & 1) ? Vs0 : Vs1, VL::PITCH);
-                if (t + 2 < n_tiles) {
-                    load_part(kreg, Kb, p.k_s[2], (t + 2) * BN);
-                    load_part(vreg, Vb, p.v_s[2], (t + 2) * BN);
-                }
-            }
-            __syncthreads();
+        }
+        end_step(t);
+    };
+
+    // prologue: the first PK K tiles and PV V tiles
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        if (u < PK && u < n_tiles) issue_k(u, kbuf_dyn(u));
+        if (u < PV && u < n_tiles) issue_v(u, vbuf_dyn(u));
+    }
+    wait_loads();
+    __syncthreads();
+    if (PIPE) {
+        if (t_last >= 0) score_products(sa, Ks0, 0, NP);
+        __syncthreads();  // K of tile 0 is read before tile NB replaces it
+    }
+    for (int t0 = 0; t0 < n_tiles; t0 += NB) {
+        step(t0, std::integral_constant<int, 0>{});
+        if (t0 + 1 < n_tiles) step(t0 + 1, std::integral_constant<int, 1>{});
+        if (NB > 2) {
+            if (t0 + 2 < n_tiles) step(t0 + 2, std::integral_constant<int, 2 % NB>{});
+            if (t0 + 3 < n_tiles) step(t0 + 3, std::integral_constant<int, 3 % NB>{});
         }
     }
 
@@ -465,43 +674,40 @@ fwd_bf16_kernel(const FwdParams p)
     }
 }
 
-template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, bool DIRECT>
+template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB>
 hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
 {
     const dim3 grid((unsigned)p.n_qtiles * p.Hq * p.B);
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, DIRECT>), grid, dim3(NW * 64), 0, st, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB>), grid, dim3(NW * 64), 0, st, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
 // Launch shapes per head dimension and mask use: waves per work-group, keys
-// per tile, waves per SIMD, direct global -> LDS staging.  Eight waves of 32
-// rows share each staged K/V tile where the registers allow two waves per
-// SIMD; at D = 256 the output accumulator alone is 128 registers per lane, so
-// that size runs four waves at one per SIMD.  Overridable at build time for
-// tuning sweeps.
+// per tile, waves per SIMD, pipelined (1) or not (0), LDS ring depth (2 or
+// 4).  Overridable at build time for tuning sweeps.
 #ifndef FA_BF16_D64_CFG
-#define FA_BF16_D64_CFG 4, 64, 2, false
+#define FA_BF16_D64_CFG 4, 64, 2, 1, 2
 #endif
 #ifndef FA_BF16_D64_MASKED_CFG
-#define FA_BF16_D64_MASKED_CFG 4, 64, 2, false
+#define FA_BF16_D64_MASKED_CFG 4, 64, 2, 0, 2
 #endif
 #ifndef FA_BF16_D128_CFG
-#define FA_BF16_D128_CFG 8, 64, 2, true
+#define FA_BF16_D128_CFG 8, 64, 2, 0, 2
 #endif
 #ifndef FA_BF16_D128_MASKED_CFG
-#define FA_BF16_D128_MASKED_CFG 8, 64, 2, false
+#define FA_BF16_D128_MASKED_CFG 8, 64, 2, 0, 2
 #endif
 #ifndef FA_BF16_D256_CFG
-#define FA_BF16_D256_CFG 4, 32, 1, false
+#define FA_BF16_D256_CFG 4, 32, 1, 0, 2
 #endif
 #ifndef FA_BF16_D256_MASKED_CFG
-#define FA_BF16_D256_MASKED_CFG 4, 32, 1, false
+#define FA_BF16_D256_MASKED_CFG 4, 32, 1, 0, 2
 #endif
 
-#define FA_BF16_VARIANT(D, MASK, CAUSAL, NAME, NW, BN, WPE, DIRECT) \
-    {NAME, 1, D, MASK, CAUSAL, NW * 32, &launch_bf16<D, MASK, CAUSAL, NW, BN, WPE, DIRECT>}
+#define FA_BF16_VARIANT(D, MASK, CAUSAL, NAME, NW, BN, WPE, SCHED, NB) \
+    {NAME, 1, D, MASK, CAUSAL, NW * 32, &launch_bf16<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB>}
 // expands a CFG macro into separate arguments before FA_BF16_VARIANT sees them
 #define FA_BF16_VARIANT_CFG(...) FA_BF16_VARIANT(__VA_ARGS__)
 
