@@ -341,7 +341,44 @@ fwd_bf16_kernel(const FwdParams p)
 
     // ---- scores of key tile j0 -> base 2, excluded keys at -inf: keys past
     // kL, keys after the row (causal), and the user mask ----
-    auto apply_mask = [&](f32x16 (&s)[NC], int j0) __attribute__((always_inline)) {
+    // Raw mask words of one key tile for this lane: for 32-key block c and
+    // quad rq, the 4 keys j0 + 32c + 8rq + 4g + {0..3} (bf16 bit pairs in x
+    // and y for an additive mask; one byte each in x for a bool mask, nonzero
+    // = attend).  Loaded one tile ahead so the global load latency is
+    // covered by a tile of work.
+    typedef u32x2 MaskWords[NC][4];
+    auto load_mask = [&](int j0, MaskWords& mw) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int jb = j0 + 32 * c + 8 * rq + 4 * g;  // first of 4 consecutive keys
+                u32x2 w = {0u, 0u};
+                if (MASK == MASK_ADD) {
+                    if (p.mask_vec && jb + 3 < p.kL) {
+                        w = *(const u32x2*)(mrow + 2 * (int64_t)jb);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (jb + e < p.kL) w[e >> 1] |= (uint32_t)((const uint16_t*)mrow)[jb + e] << (16 * (e & 1));
+                    }
+                } else if (MASK == MASK_BOOL) {
+                    if (p.mask_vec && jb + 3 < p.kL) {
+                        w[0] = *(const uint32_t*)(mrow + jb);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (jb + e < p.kL && mrow[jb + e] != 0) w[0] |= 1u << (8 * e);
+                    }
+                }
+                mw[c][rq] = w;
+            }
+        }
+    };
+
+    // ---- scores of key tile j0 -> base 2, excluded keys at -inf: keys past
+    // kL, keys after the row (causal), and the user mask (its words in mw) ----
+    auto apply_mask = [&](f32x16 (&s)[NC], int j0, const MaskWords& mw) __attribute__((always_inline)) {
         if (MASK == MASK_NONE) {
             // key j0 + 32c + 8rq + 4g + e is allowed iff 32c + 8rq + e <= lim
             int lim = p.kL - 1;
@@ -358,38 +395,19 @@ fwd_bf16_kernel(const FwdParams p)
         for (int c = 0; c < NC; ++c) {
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
-                const int jb = j0 + 32 * c + 8 * rq + 4 * g;  // first of 4 consecutive keys
-                float mv[4] = {0.f, 0.f, 0.f, 0.f};
-                bool mb[4] = {true, true, true, true};
-                if (MASK == MASK_ADD) {
-                    if (p.mask_vec && jb + 3 < p.kL) {
-                        const u32x2 w = *(const u32x2*)(mrow + 2 * (int64_t)jb);
-                        mv[0] = bf16_bits_to_float(w[0] & 0xffffu);
-                        mv[1] = bf16_bits_to_float(w[0] >> 16);
-                        mv[2] = bf16_bits_to_float(w[1] & 0xffffu);
-                        mv[3] = bf16_bits_to_float(w[1] >> 16);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (jb + e < p.kL) mv[e] = bf16_bits_to_float(((const uint16_t*)mrow)[jb + e]);
-                    }
-                } else {
-                    if (p.mask_vec && jb + 3 < p.kL) {
-                        const uint32_t w = *(const uint32_t*)(mrow + jb);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) mb[e] = ((w >> (8 * e)) & 0xffu) != 0;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) mb[e] = (jb + e < p.kL) ? (mrow[jb + e] != 0) : false;
-                    }
-                }
+                const int jb = j0 + 32 * c + 8 * rq + 4 * g;
+                const u32x2 w = mw[c][rq];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int j = jb + e;
-                    bool ok = (j < p.kL) && mb[e];
+                    bool ok = j < p.kL;
+                    if (MASK == MASK_BOOL) ok = ok && ((w[0] >> (8 * e)) & 0xffu) != 0;
                     if (CAUSAL) ok = ok && (j <= qrow);
                     float x = s[c][4 * rq + e] * c2;
-                    if (MASK == MASK_ADD) x = __builtin_fmaf(mv[e], kLog2e, x);
+                    if (MASK == MASK_ADD) {
+                        const uint32_t bits = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                        x = __builtin_fmaf(bf16_bits_to_float(bits), kLog2e, x);
+                    }
                     s[c][4 * rq + e] = ok ? x : -INFINITY;
                 }
             }
@@ -567,14 +585,14 @@ fwd_bf16_kernel(const FwdParams p)
     };
 
     // softmax and P V of tile t with its scores in s
-    auto finish_tile = [&](int t, f32x16 (&s)[NC], const uint16_t* vt, f32x16 (&sn)[NC], const uint16_t* kn)
-        __attribute__((always_inline)) {
+    auto finish_tile = [&](int t, f32x16 (&s)[NC], const uint16_t* vt, f32x16 (&sn)[NC], const uint16_t* kn,
+                           const MaskWords& mw) __attribute__((always_inline)) {
         const int j0 = t * BN;
         const bool masked = (MASK != MASK_NONE) || (j0 + BN > p.kL) || (CAUSAL && j0 + BN - 1 > wq0);
         // one softmax for both kinds of tile, so that the accumulators and
         // the next tile's scores are written in one place (two copies of the
         // softmax would make the register allocator move them at the join)
-        if (masked) apply_mask(s, j0);
+        if (masked) apply_mask(s, j0, mw);
         const float cs = masked ? 1.f : c2;
         if (SCHED == 0) {
             softmax_pv(s, cs, vt, sn, kn, std::integral_constant<int, 0>{});
@@ -610,12 +628,16 @@ fwd_bf16_kernel(const FwdParams p)
             wait_loads();
         __syncthreads();
     };
+    MaskWords ma, mb;  // mask words of the current and the next tile
     auto step = [&](int t, auto u_c) __attribute__((always_inline)) {
         constexpr int U = decltype(u_c)::value;  // t % NB
         f32x16(&sc)[NC] = (U & 1) ? sb : sa;
         f32x16(&sn)[NC] = (U & 1) ? sa : sb;
+        MaskWords& mc = (U & 1) ? mb : ma;
+        MaskWords& mn = (U & 1) ? ma : mb;
         if (t + PK < n_tiles) issue_k(t + PK, kbuf(std::integral_constant<int, (U + PK) % NB>{}));
         if (t + PV < n_tiles) issue_v(t + PV, vbuf(std::integral_constant<int, (U + PV) % NB>{}));
+        if (MASK != MASK_NONE && t + 1 <= t_last) load_mask((t + 1) * BN, mn);
         if (t <= t_last) {
             const uint16_t* vr = vbuf(std::integral_constant<int, U>{});
             if (PIPE) {
@@ -623,11 +645,11 @@ fwd_bf16_kernel(const FwdParams p)
                 // whatever its K buffer holds): keeping them unconditional
                 // keeps them in the same instruction stream as this softmax,
                 // and a result that is not needed is never read
-                finish_tile(t, sc, vr, sn, kbuf(std::integral_constant<int, (U + 1) % NB>{}));
+                finish_tile(t, sc, vr, sn, kbuf(std::integral_constant<int, (U + 1) % NB>{}), mc);
             } else {
                 const uint16_t* kr = kbuf(std::integral_constant<int, U>{});
                 score_products(sa, kr, 0, NP);
-                finish_tile(t, sa, vr, sb, kr);
+                finish_tile(t, sa, vr, sb, kr, mc);
             }
         }
         end_step(t);
@@ -639,6 +661,7 @@ fwd_bf16_kernel(const FwdParams p)
         if (u < PK && u < n_tiles) issue_k(u, kbuf_dyn(u));
         if (u < PV && u < n_tiles) issue_v(u, vbuf_dyn(u));
     }
+    if (MASK != MASK_NONE && t_last >= 0) load_mask(0, ma);
     wait_loads();
     __syncthreads();
     if (PIPE) {
