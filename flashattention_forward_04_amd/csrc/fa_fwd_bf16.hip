@@ -59,6 +59,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -162,7 +163,7 @@ __device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
 // tile ahead of V.
 //
 // K/V tiles are loaded straight from global memory into LDS (no registers),
-// double-buffered, with one barrier per tile.
+// round a ring of NB buffers, with one barrier per tile.
 template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fwd_bf16_kernel(const FwdParams p)
@@ -705,6 +706,333 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Key-split forward for few, wide rows.  At D = 256 a wave needs a whole SIMD
+// of registers, so a launch with fewer than one work-group per CU leaves most
+// SIMDs idle (an 8-head 1024-row problem has 256 waves of 32 rows for 1024
+// SIMDs).  Here a work-group owns only 32 query rows and its NS waves split
+// the key range instead (wave w takes key tiles w, w + NS, ...), each with
+// its own LDS buffers and no barrier in the loop.  The waves' partial
+// softmax states are merged through LDS at the end -- the same merge of
+// (O, m, l) partials that combines key blocks in the online softmax -- so no
+// scratch memory is needed.
+//
+// Per tile a wave loads K (and the mask words) ahead of V: the K buffer is
+// refilled as soon as the score operands are in registers, the V buffer as
+// soon as the P V operands are, so each load has a softmax or a score phase
+// to land in.
+template <int D, int MASK, bool CAUSAL, int NS, int BN>
+__global__ void __launch_bounds__(NS * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+fwd_bf16_split_kernel(const FwdParams p)
+{
+    using KL = TileLayout<D + 8>;
+    using VL = TileLayout<D + 32>;
+    constexpr int KSPR = KL::PITCH / 8;
+    constexpr int VSPR = VL::PITCH / 8;
+    constexpr int KINS = (BN * KSPR + 63) / 64;  // 1 KiB blocks (and loads) per K tile
+    constexpr int VINS = (BN * VSPR + 63) / 64;  // 1 KiB blocks (and loads) per V tile
+    constexpr int KTILE = KINS * 512;
+    constexpr int VTILE = VINS * 512;
+    constexpr int DK = D / 16;
+    constexpr int NC = BN / 32;
+    constexpr int ND = D / 32;
+    constexpr int OPITCH = D + 4;                // floats per row of a partial O in LDS
+    constexpr int NMASK = (MASK == MASK_NONE) ? 0 : NC * 4;  // mask loads per tile (vector path)
+    static_assert(NS == 4 && ND % NS == 0, "the merge gives each wave ND / NS blocks of O");
+    static_assert(2 * 32 * OPITCH * 4 <= NS * KTILE * 2 && 2 * 32 * OPITCH * 4 <= NS * VTILE * 2,
+                  "two partial O tiles fit in each of the K and V areas");
+    static_assert(KINS < 48 && VINS + NMASK < 48, "vmcnt range");
+
+    __shared__ __attribute__((aligned(1024))) uint16_t Kall[NS * KTILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vall[NS * VTILE];
+    __shared__ float Mpart[NS][32];
+    __shared__ float Lpart[NS][32];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r32 = lane & 31;
+    const int g = lane >> 5;
+
+    int id = blockIdx.x;
+    const int h = head_of(id % p.Hq, p.Hq);
+    id /= p.Hq;
+    const int b = id % p.B;
+    id /= p.B;
+    const int qt = CAUSAL ? (p.n_qtiles - 1 - id) : id;
+    const int q0 = qt * 32;
+    const int qrow = q0 + r32;
+    const int hk = h / p.group;
+
+    const uint16_t* Qb = (const uint16_t*)p.q + b * p.q_s[0] + h * p.q_s[1];
+    const uint16_t* Kb = (const uint16_t*)p.k + b * p.k_s[0] + hk * p.k_s[1];
+    const uint16_t* Vb = (const uint16_t*)p.v + b * p.v_s[0] + hk * p.v_s[1];
+
+    bf16x8 qf[DK];
+    {
+        const bool in = qrow < p.qL;
+        const u32x4* src = (const u32x4*)(Qb + (int64_t)(in ? qrow : 0) * p.q_s[2]);
+        const uint32_t flip = p.neg_q ? 0x80008000u : 0u;
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) {
+            u32x4 w = in ? src[2 * ks + g] : u32x4{0, 0, 0, 0};
+            w ^= flip;
+            qf[ks] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+    const float c2 = p.scale_log2;
+    const int kv_end = CAUSAL ? min(p.kL, min(p.qL, q0 + 32)) : p.kL;
+    const int n_tiles = (q0 < p.qL) ? (kv_end + BN - 1) / BN : 0;
+
+    const uint8_t* mrow = nullptr;
+    if (MASK != MASK_NONE) {
+        const int qc = min(qrow, p.qL - 1);
+        const int esz = (MASK == MASK_BOOL) ? 1 : 2;
+        mrow = (const uint8_t*)p.mask + (b * p.m_s[0] + h * p.m_s[1] + (int64_t)qc * p.m_s[2]) * esz;
+    }
+
+    f32x16 o[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) o[d] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    uint16_t* Kw = Kall + wave * KTILE;
+    uint16_t* Vw = Vall + wave * VTILE;
+    // the whole tile by this wave: block i is one direct load (see the
+    // work-group kernel); rows past kL load row kL - 1
+    auto issue_tile = [&](const uint16_t* gbase, int64_t stride, int j0, uint16_t* lds, auto spr_c, auto nins_c)
+        __attribute__((always_inline)) {
+        constexpr int SPR = decltype(spr_c)::value;
+        constexpr int NINS = decltype(nins_c)::value;
+#pragma unroll
+        for (int i = 0; i < NINS; ++i) {
+            const int slot = 64 * i + lane;
+            const int row = slot / SPR;
+            const int ch = slot % SPR;
+            if (ch < D / 8 && row < BN) {
+                const int j = min(j0 + row, p.kL - 1);
+                lds_dma16(gbase + (int64_t)j * stride + ch * 8,
+                          (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(lds + 512 * i));
+            }
+        }
+    };
+
+    typedef u32x2 MaskWords[NC][4];
+    auto load_mask = [&](int j0, MaskWords& mw) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int jb = j0 + 32 * c + 8 * rq + 4 * g;
+                u32x2 w = {0u, 0u};
+                if (MASK == MASK_ADD) {
+                    if (p.mask_vec && jb + 3 < p.kL) {
+                        w = *(const u32x2*)(mrow + 2 * (int64_t)jb);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (jb + e < p.kL) w[e >> 1] |= (uint32_t)((const uint16_t*)mrow)[jb + e] << (16 * (e & 1));
+                    }
+                } else if (MASK == MASK_BOOL) {
+                    if (p.mask_vec && jb + 3 < p.kL) {
+                        w[0] = *(const uint32_t*)(mrow + jb);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (jb + e < p.kL && mrow[jb + e] != 0) w[0] |= 1u << (8 * e);
+                    }
+                }
+                mw[c][rq] = w;
+            }
+        }
+    };
+    // K (and the mask words) of tile t, then V of tile t
+    auto issue_k = [&](int t, MaskWords& mw) __attribute__((always_inline)) {
+        issue_tile(Kb, p.k_s[2], t * BN, Kw, std::integral_constant<int, KSPR>{}, std::integral_constant<int, KINS>{});
+        if (MASK != MASK_NONE) load_mask(t * BN, mw);
+    };
+    auto issue_v = [&](int t) __attribute__((always_inline)) {
+        issue_tile(Vb, p.v_s[2], t * BN, Vw, std::integral_constant<int, VSPR>{}, std::integral_constant<int, VINS>{});
+    };
+
+    MaskWords mw, mwn;
+    int t = wave;
+    if (t < n_tiles) {
+        issue_k(t, mw);
+        issue_v(t);
+    }
+    const int lt = lane & 15;
+    for (; t < n_tiles; t += NS) {
+        const int tn = t + NS;
+        const int j0 = t * BN;
+        // K and the mask words of tile t have landed (V, issued after them,
+        // may still be in flight)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (VINS & 15) | ((VINS >> 4) << 14));
+        f32x16 s[NC];
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const bf16x8 kop = *(const bf16x8*)(Kw + KL::off(32 * c + r32, 2 * ks + g));
+                s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[ks], ks == 0 ? f32x16{} : s[c], 0, 0, 0);
+            }
+        // the score operands are in registers: refill the K buffer
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        if (tn < n_tiles) issue_k(tn, mwn);
+
+        const bool masked = (MASK != MASK_NONE) || (j0 + BN > p.kL) || (CAUSAL && j0 + BN - 1 > q0);
+        if (masked) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int jb = j0 + 32 * c + 8 * rq + 4 * g;
+                    const u32x2 w = mw[c][rq];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = jb + e;
+                        bool ok = j < p.kL;
+                        if (MASK == MASK_BOOL) ok = ok && ((w[0] >> (8 * e)) & 0xffu) != 0;
+                        if (CAUSAL) ok = ok && (j <= qrow);
+                        float x = s[c][4 * rq + e] * c2;
+                        if (MASK == MASK_ADD) {
+                            const uint32_t bits = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                            x = __builtin_fmaf(bf16_bits_to_float(bits), kLog2e, x);
+                        }
+                        s[c][4 * rq + e] = ok ? x : -INFINITY;
+                    }
+                }
+        }
+        const float cs = masked ? 1.f : c2;
+        float mx = s[0][0];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c][r]);
+        const float m_tile = row_max_halves(mx) * cs;
+        if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
+            const float m_new = fmaxf(m_run, m_tile);
+            if (m_run != -INFINITY && m_new != m_run) {
+                const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= corr;
+#pragma unroll
+                for (int d = 0; d < ND; ++d) o[d] *= corr;
+            }
+            m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        // V of tile t has landed (only K and mask words of tile tn are newer)
+        if (tn < n_tiles)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | ((KINS + NMASK) & 15) | (((KINS + NMASK) >> 4) << 14));
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+        float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int kidx = 2 * c + hh;
+                u32x4 pw;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][8 * hh + 2 * e], cs, -m_use));
+                    const float z = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][8 * hh + 2 * e + 1], cs, -m_use));
+                    pw[e] = pack_bf16x2(a, z);
+                    rs0 += a;
+                    rs1 += z;
+                }
+                const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+                for (int d = 0; d < ND; ++d) {
+                    const int col = 32 * d + 16 * ((lane >> 4) & 1) + 4 * (lt & 3);
+                    const int row0 = 16 * kidx + 4 * g + (lt >> 2);
+                    const i16x4 v0 = lds_read_tr(Vw + VL::off(row0, 0) + col);
+                    const i16x4 v1 = lds_read_tr(Vw + VL::off(row0 + 8, 0) + col);
+                    const bf16x8 vop =
+                        __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+                    o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pf, o[d], 0, 0, 0);
+                }
+            }
+        }
+        l_run += row_sum_halves(rs0 + rs1);
+        // the P V operands are in registers: refill the V buffer
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        if (tn < n_tiles) issue_v(tn);
+        if (MASK != MASK_NONE) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) mw[c][rq] = mwn[c][rq];
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // no load of this wave is still writing LDS
+
+    // ---- merge the NS partial softmax states of each row ----
+    __syncthreads();  // every wave is done with its K and V buffers
+    if (g == 0) Mpart[wave][r32] = m_run;
+    __syncthreads();
+    float m_fin = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NS; ++w) m_fin = fmaxf(m_fin, Mpart[w][r32]);
+    const float corr = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_fin);
+    float* opart = (wave < 2) ? (float*)Kall + wave * (32 * OPITCH) : (float*)Vall + (wave - 2) * (32 * OPITCH);
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            f32x4 v = {o[d][4 * rq] * corr, o[d][4 * rq + 1] * corr, o[d][4 * rq + 2] * corr, o[d][4 * rq + 3] * corr};
+            *(f32x4*)(opart + r32 * OPITCH + 32 * d + 8 * rq + 4 * g) = v;
+        }
+    if (g == 0) Lpart[wave][r32] = l_run * corr;
+    __syncthreads();
+    float l_fin = 0.f;
+#pragma unroll
+    for (int w = 0; w < NS; ++w) l_fin += Lpart[w][r32];
+    if (qrow < p.qL) {
+        const float inv = (l_fin > 0.f) ? 1.f / l_fin : 0.f;
+        uint16_t* orow = (uint16_t*)p.o + b * p.o_s[0] + h * p.o_s[1] + (int64_t)qrow * p.o_s[2];
+        // wave w finishes head-dimension blocks [w ND/NS, (w+1) ND/NS)
+#pragma unroll
+        for (int dd = 0; dd < ND / NS; ++dd) {
+            const int d = wave * (ND / NS) + dd;
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int off = r32 * OPITCH + 32 * d + 8 * rq + 4 * g;
+                f32x4 acc = *(const f32x4*)((float*)Kall + off);
+                acc += *(const f32x4*)((float*)Kall + 32 * OPITCH + off);
+                acc += *(const f32x4*)((float*)Vall + off);
+                acc += *(const f32x4*)((float*)Vall + 32 * OPITCH + off);
+                u32x2 w;
+                w[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+                w[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+                *(u32x2*)(orow + 32 * d + 8 * rq + 4 * g) = w;
+            }
+        }
+        if (wave == 0 && g == 0) {
+            const float lse = (l_fin > 0.f) ? (m_fin + __builtin_amdgcn_logf(l_fin)) * kLn2 : 0.f;
+            p.lse[((int64_t)b * p.Hq + h) * p.qL + qrow] = lse;
+        }
+    }
+}
+
+// Launch: the work-group kernel, or for wide rows whose grid would not give
+// every CU a work-group, the key-split kernel
+// (D = 256 only: narrower rows leave room for more waves per SIMD instead.)
+template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB>
+hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
+{
+    if constexpr (D == 256) {
+        constexpr int kCUs = 256;
+        if ((int64_t)p.n_qtiles * p.Hq * p.B < kCUs) {
+            FwdParams q = p;
+            q.n_qtiles = (p.qL + 31) / 32;
+            const dim3 grid((unsigned)q.n_qtiles * q.Hq * q.B);
+            hipLaunchKernelGGL((fwd_bf16_split_kernel<D, MASK, CAUSAL, 4, 32>), grid, dim3(4 * 64), 0, st, q);
+            return hipGetLastError();
+        }
+    }
+    return launch_bf16<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB>(p, st);
+}
+
 }  // namespace
 
 // Launch shapes per head dimension and mask use: waves per work-group, keys
@@ -730,7 +1058,7 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
 #endif
 
 #define FA_BF16_VARIANT(D, MASK, CAUSAL, NAME, NW, BN, WPE, SCHED, NB) \
-    {NAME, 1, D, MASK, CAUSAL, NW * 32, &launch_bf16<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB>}
+    {NAME, 1, D, MASK, CAUSAL, NW * 32, &launch_bf16_any<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB>}
 // expands a CFG macro into separate arguments before FA_BF16_VARIANT sees them
 #define FA_BF16_VARIANT_CFG(...) FA_BF16_VARIANT(__VA_ARGS__)
 

@@ -114,6 +114,45 @@ def test_masks(dtype, kind, causal):
     assert np.all(O[0, 1, 5] == 0) and L[0, 1, 5] == 0, "row with no allowed key is not O = 0, L = 0"
 
 
+@pytest.mark.parametrize("kind", ["none", "additive", "bool"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_wide_rows_key_split(kind, causal):
+    """D = 256 bf16 with too few query tiles to give every CU a work-group:
+    the key range is split across a work-group's waves and merged in LDS.
+    Ragged lengths, a key count that is not a multiple of any tile, and a
+    masked row with no allowed key."""
+    qL, kL = 100, 333
+    q, k, v = _rand((1, 3, qL, 256), BF16, 21), _rand((1, 3, kL, 256), BF16, 22), _rand((1, 3, kL, 256), BF16, 23)
+    mask = None
+    if kind != "none":
+        rng = np.random.default_rng(24)
+        masked = W.draw_masked(rng, (1, 3, qL, kL), 0.25)
+        masked[0, 2, 7, :] = True
+        if kind == "bool":
+            mask = torch.from_numpy((~masked).astype(np.uint8))
+        else:
+            m = rng.standard_normal(masked.shape).astype(np.float32)
+            m[masked] = -np.inf
+            mask = torch.from_numpy(m).to(BF16)
+    O, L, _ = run_gpu(q, k, v, mask, causal=causal, scale=1 / 16)
+    Oref, Lref = run_oracle(q, k, v, mask, causal=causal, scale=1 / 16)
+    assert_parity(O, L, Oref, Lref, "bf16", f"D=256 key split {kind} causal={causal}")
+    if kind != "none":
+        assert np.all(O[0, 2, 7] == 0) and L[0, 2, 7] == 0, "row with no allowed key is not O = 0, L = 0"
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_wide_rows_work_group_path(causal):
+    """D = 256 bf16 with a grid that fills the GPU (16 heads x 16 tiles of 128
+    rows): the work-group kernel, not the key split; oracle on sampled rows."""
+    w = W.Workload("d256_wg_path", "bf16", 1, 16, 4, 2048, 2048, 256, 1 / 16, causal=causal, seed=25)
+    q, k, v, _ = _draw(w)
+    O, L, _ = run_gpu(q, k, v, None, causal=causal, scale=w.scale)
+    rows = W.sample_rows(w, 384)
+    Oref, Lref = run_oracle(q, k, v, None, causal=causal, scale=w.scale, rows=rows)
+    assert_parity(O.reshape(-1, 256)[rows], L.reshape(-1)[rows], Oref, Lref, "bf16", w.name + " sampled")
+
+
 def test_bool_mask_equals_additive():
     q, k, v = _rand((1, 2, 64, 128), BF16, 8), _rand((1, 2, 96, 128), BF16, 9), _rand((1, 2, 96, 128), BF16, 10)
     attend = torch.from_numpy(np.random.default_rng(11).random((1, 2, 64, 96)) < 0.5)
