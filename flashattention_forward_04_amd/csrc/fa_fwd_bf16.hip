@@ -349,28 +349,27 @@ fwd_bf16_kernel(const FwdParams p)
     // covered by a tile of work.
     typedef u32x2 MaskWords[NC][4];
     auto load_mask = [&](int j0, MaskWords& mw) __attribute__((always_inline)) {
+        // one decision per tile (a per-quad one would split the loads into
+        // branches the compiler's wait counting merges pessimistically)
+        const bool vec = p.mask_vec && j0 + BN <= p.kL;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
                 const int jb = j0 + 32 * c + 8 * rq + 4 * g;  // first of 4 consecutive keys
                 u32x2 w = {0u, 0u};
-                if (MASK == MASK_ADD) {
-                    if (p.mask_vec && jb + 3 < p.kL) {
-                        w = *(const u32x2*)(mrow + 2 * (int64_t)jb);
-                    } else {
+                if (vec) {
+                    // whole tile inside the row, rows aligned: one load per quad
+                    if (MASK == MASK_ADD) w = *(const u32x2*)(mrow + 2 * (int64_t)jb);
+                    if (MASK == MASK_BOOL) w[0] = *(const uint32_t*)(mrow + jb);
+                } else if (MASK == MASK_ADD) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (jb + e < p.kL) w[e >> 1] |= (uint32_t)((const uint16_t*)mrow)[jb + e] << (16 * (e & 1));
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        if (jb + e < p.kL) w[e >> 1] |= (uint32_t)((const uint16_t*)mrow)[jb + e] << (16 * (e & 1));
                 } else if (MASK == MASK_BOOL) {
-                    if (p.mask_vec && jb + 3 < p.kL) {
-                        w[0] = *(const uint32_t*)(mrow + jb);
-                    } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (jb + e < p.kL && mrow[jb + e] != 0) w[0] |= 1u << (8 * e);
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        if (jb + e < p.kL && mrow[jb + e] != 0) w[0] |= 1u << (8 * e);
                 }
                 mw[c][rq] = w;
             }
@@ -798,7 +797,10 @@ fwd_bf16_split_kernel(const FwdParams p)
     uint16_t* Kw = Kall + wave * KTILE;
     uint16_t* Vw = Vall + wave * VTILE;
     // the whole tile by this wave: block i is one direct load (see the
-    // work-group kernel); rows past kL load row kL - 1
+    // work-group kernel); rows past kL load row kL - 1.  Here the compiler
+    // tracks the loads: the mask words are ordinary loads, and a wait for
+    // them would otherwise also wait for every untracked load issued after
+    // them, i.e. for the next K tile.
     auto issue_tile = [&](const uint16_t* gbase, int64_t stride, int j0, uint16_t* lds, auto spr_c, auto nins_c)
         __attribute__((always_inline)) {
         constexpr int SPR = decltype(spr_c)::value;
@@ -810,36 +812,36 @@ fwd_bf16_split_kernel(const FwdParams p)
             const int ch = slot % SPR;
             if (ch < D / 8 && row < BN) {
                 const int j = min(j0 + row, p.kL - 1);
-                lds_dma16(gbase + (int64_t)j * stride + ch * 8,
-                          (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(lds + 512 * i));
+                __builtin_amdgcn_global_load_lds(
+                    (__attribute__((address_space(1))) void*)(gbase + (int64_t)j * stride + ch * 8),
+                    (__attribute__((address_space(3))) void*)(lds + 512 * i), 16, 0, 0);
             }
         }
     };
 
     typedef u32x2 MaskWords[NC][4];
     auto load_mask = [&](int j0, MaskWords& mw) __attribute__((always_inline)) {
+        // one decision per tile (a per-quad one would split the loads into
+        // branches the compiler's wait counting merges pessimistically)
+        const bool vec = p.mask_vec && j0 + BN <= p.kL;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
                 const int jb = j0 + 32 * c + 8 * rq + 4 * g;
                 u32x2 w = {0u, 0u};
-                if (MASK == MASK_ADD) {
-                    if (p.mask_vec && jb + 3 < p.kL) {
-                        w = *(const u32x2*)(mrow + 2 * (int64_t)jb);
-                    } else {
+                if (vec) {
+                    // whole tile inside the row, rows aligned: one load per quad
+                    if (MASK == MASK_ADD) w = *(const u32x2*)(mrow + 2 * (int64_t)jb);
+                    if (MASK == MASK_BOOL) w[0] = *(const uint32_t*)(mrow + jb);
+                } else if (MASK == MASK_ADD) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (jb + e < p.kL) w[e >> 1] |= (uint32_t)((const uint16_t*)mrow)[jb + e] << (16 * (e & 1));
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        if (jb + e < p.kL) w[e >> 1] |= (uint32_t)((const uint16_t*)mrow)[jb + e] << (16 * (e & 1));
                 } else if (MASK == MASK_BOOL) {
-                    if (p.mask_vec && jb + 3 < p.kL) {
-                        w[0] = *(const uint32_t*)(mrow + jb);
-                    } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (jb + e < p.kL && mrow[jb + e] != 0) w[0] |= 1u << (8 * e);
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        if (jb + e < p.kL && mrow[jb + e] != 0) w[0] |= 1u << (8 * e);
                 }
                 mw[c][rq] = w;
             }
@@ -875,10 +877,6 @@ fwd_bf16_split_kernel(const FwdParams p)
                 const bf16x8 kop = *(const bf16x8*)(Kw + KL::off(32 * c + r32, 2 * ks + g));
                 s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[ks], ks == 0 ? f32x16{} : s[c], 0, 0, 0);
             }
-        // the score operands are in registers: refill the K buffer
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-        if (tn < n_tiles) issue_k(tn, mwn);
-
         const bool masked = (MASK != MASK_NONE) || (j0 + BN > p.kL) || (CAUSAL && j0 + BN - 1 > q0);
         if (masked) {
 #pragma unroll
@@ -902,6 +900,12 @@ fwd_bf16_split_kernel(const FwdParams p)
                     }
                 }
         }
+        // the score operands are in registers and this tile's mask words are
+        // used: refill the K buffer (and fetch the next mask words).  Issued
+        // only now, so that the compiler's wait for this tile's mask words
+        // does not also wait for these loads.
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        if (tn < n_tiles) issue_k(tn, mwn);
         const float cs = masked ? 1.f : c2;
         float mx = s[0][0];
 #pragma unroll
