@@ -1,5 +1,5 @@
 // fa_common.h - types shared by the gfx950 forward kernels and their host
-// dispatch.  Device-side helpers live with the kernels that use them.
+// dispatch, and the device helpers both kernel files use.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,6 +40,28 @@ enum MaskKind { MASK_NONE = 0, MASK_ADD = 1, MASK_BOOL = 2 };
 // from its own L2.  Other head counts keep the plain order.
 __device__ __forceinline__ int head_of(int slot, int Hq) {
     return (Hq % 8 == 0) ? (slot % 8) * (Hq / 8) + slot / 8 : slot;
+}
+
+// One direct global -> LDS load (global_load_lds_dwordx4): lane l's 16
+// bytes land at LDS byte address lds_base + 16 l.  It is issued from inline
+// assembly so that the compiler does not track it: while a direct load it
+// knows of is in flight, the compiler turns every wait for an LDS read into
+// a wait for all of them, which serialises the operand reads with the
+// matrix products.  Completion is ordered instead by the key loop's explicit
+// vmcnt waits and barriers (a load the compiler does not know of can only
+// make its own waits wait longer).  M0 is saved and restored around it.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0"
+        : "=&s"(saved)
+        : "v"(gsrc), "s"(lds_base)
+        : "memory");
 }
 
 // One compiled variant: its launch function and shape facts the host needs.

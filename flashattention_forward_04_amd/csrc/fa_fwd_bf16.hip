@@ -119,28 +119,6 @@ struct TileLayout {
     __device__ static __forceinline__ int off(int row, int chunk) { return row * P + chunk * 8; }
 };
 
-// One direct global -> LDS load (global_load_lds_dwordx4): lane l's 16
-// bytes land at LDS byte address lds_base + 16 l.  It is issued from inline
-// assembly so that the compiler does not track it: while a direct load it
-// knows of is in flight, the compiler turns every wait for an LDS read into
-// a wait for all of them, which serialises the operand reads with the
-// matrix products.  Completion is ordered instead by the key loop's explicit
-// vmcnt waits and barriers (a load the compiler does not know of can only
-// make its own waits wait longer).  M0 is saved and restored around it.
-__device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_base) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0\n\t"
-        "s_nop 0"
-        : "=&s"(saved)
-        : "v"(gsrc), "s"(lds_base)
-        : "memory");
-}
-
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 

@@ -50,12 +50,18 @@ fwd_f32_kernel(const FwdParams p)
     constexpr int ND = D / 32;
     static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) float Ks[BN * KP];
-    __shared__ __attribute__((aligned(16))) float Vt[D * VP];
+    // two buffers each: K row-major (filled by direct global -> LDS loads,
+    // padded to whole 1 KiB blocks) and V transposed (filled from registers)
+    constexpr int KSPR = KP / 4;                 // 16-byte slots per K row
+    constexpr int KINS = (BN * KSPR + 63) / 64;  // 1 KiB blocks per K tile
+    __shared__ __attribute__((aligned(1024))) float Ks0[KINS * 256];
+    __shared__ __attribute__((aligned(1024))) float Ks1[KINS * 256];
+    __shared__ __attribute__((aligned(16))) float Vt0[D * VP];
+    __shared__ __attribute__((aligned(16))) float Vt1[D * VP];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r32 = lane & 31;
     const int g = lane >> 5;
 
@@ -100,44 +106,8 @@ fwd_f32_kernel(const FwdParams p)
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    for (int j0 = 0; j0 < kv_end; j0 += BN) {
-        __syncthreads();
-        // ---- stage K row-major ----
-        constexpr int KCH = BN * D / 4;
-#pragma unroll
-        for (int it = 0; it < (KCH + NT - 1) / NT; ++it) {
-            const int c = tid + it * NT;
-            if (KCH % NT != 0 && c >= KCH) break;
-            const int row = c / (D / 4);
-            const int col = c % (D / 4);
-            const int j = j0 + row;
-            f32x4 w = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (j < p.kL) w = *(const f32x4*)(Kb + (int64_t)j * p.k_s[2] + col * 4);
-            *(f32x4*)(Ks + row * KP + col * 4) = w;
-        }
-        // ---- stage V transposed: Vt[d][j], 4 keys x 4 dims per unit ----
-        constexpr int VU = (BN / 4) * (D / 4);
-#pragma unroll
-        for (int it = 0; it < (VU + NT - 1) / NT; ++it) {
-            const int u = tid + it * NT;
-            if (VU % NT != 0 && u >= VU) break;
-            const int w4 = u % (D / 4);
-            const int qd = u / (D / 4);
-            f32x4 r[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = j0 + 4 * qd + e;
-                r[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (j < p.kL) r[e] = *(const f32x4*)(Vb + (int64_t)j * p.v_s[2] + w4 * 4);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *(f32x4*)(Vt + (4 * w4 + i) * VP + 4 * qd) = f32x4{r[0][i], r[1][i], r[2][i], r[3][i]};
-        }
-        __syncthreads();
-
-        if (CAUSAL && j0 > wq0 + 31) continue;
-
+    // ---- one key tile: j0, its K (row-major) and V^T staged at Ks, Vt ----
+    auto tile = [&](int j0, const float* Ks, const float* Vt) __attribute__((always_inline)) {
         // ---- S^T = K Q^T ----
         f32x16 s[NC];
 #pragma unroll
@@ -235,6 +205,94 @@ fwd_f32_kernel(const FwdParams p)
                 }
             }
         }
+    };
+
+    const int n_tiles = (kv_end + BN - 1) / BN;
+    // this wave needs tiles 0..t_last (causal rows never see later keys)
+    int t_last = n_tiles - 1;
+    if (CAUSAL) t_last = min(t_last, (wq0 + 31) / BN);
+
+    // K tile t -> LDS directly: 1 KiB block i by wave i % NW, lane l writing
+    // slot 64i + l; pad slots are skipped, rows past kL repeat row kL - 1
+    auto issue_k = [&](int t, float* kt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < (KINS + NW - 1) / NW; ++k) {
+            const int i = wave + k * NW;
+            if (KINS % NW != 0 && i >= KINS) break;
+            const int slot = 64 * i + lane;
+            const int row = slot / KSPR;
+            const int ch = slot % KSPR;
+            if (ch < D / 4 && row < BN) {
+                const int j = min(t * BN + row, p.kL - 1);
+                const float* src = Kb + (int64_t)j * p.k_s[2] + ch * 4;
+                if (MASK == MASK_NONE) {
+                    lds_dma16(src, (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(kt + 256 * i));
+                } else {
+                    // tracked by the compiler: the mask loads' waits count exactly
+                    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                                     (__attribute__((address_space(3))) void*)(kt + 256 * i), 16, 0,
+                                                     0);
+                }
+            }
+        }
+    };
+    // V tile t -> registers (4 keys x 4 dims per unit), stored transposed
+    // into LDS once the current tile is done with the other buffer
+    constexpr int VU = (BN / 4) * (D / 4);
+    constexpr int VIT = (VU + NT - 1) / NT;
+    f32x4 vr[VIT][4];
+    auto load_v = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < VIT; ++it) {
+            const int u = tid + it * NT;
+            if (VU % NT != 0 && u >= VU) break;
+            const int w4 = u % (D / 4);
+            const int qd = u / (D / 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = min(t * BN + 4 * qd + e, p.kL - 1);
+                vr[it][e] = *(const f32x4*)(Vb + (int64_t)j * p.v_s[2] + w4 * 4);
+            }
+        }
+    };
+    auto store_v = [&](float* vt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < VIT; ++it) {
+            const int u = tid + it * NT;
+            if (VU % NT != 0 && u >= VU) break;
+            const int w4 = u % (D / 4);
+            const int qd = u / (D / 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *(f32x4*)(vt + (4 * w4 + i) * VP + 4 * qd) =
+                    f32x4{vr[it][0][i], vr[it][1][i], vr[it][2][i], vr[it][3][i]};
+        }
+    };
+
+    // tile 0, then the loop: tile t+1 is loaded (K straight into LDS, V into
+    // registers) while tile t is computed; V goes to LDS after tile t
+    issue_k(0, Ks0);
+    load_v(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    store_v(Vt0);
+    __syncthreads();
+    auto step = [&](int t, const float* Ks, const float* Vt, float* kn, float* vn) __attribute__((always_inline)) {
+        const int j0 = t * BN;
+        const bool more = t + 1 < n_tiles;
+        if (more) {
+            issue_k(t + 1, kn);
+            load_v(t + 1);
+        }
+        if (t <= t_last) {
+            tile(j0, Ks, Vt);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K of tile t+1 in LDS, V in registers
+        if (more) store_v(vn);
+        __syncthreads();
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+        step(t, Ks0, Vt0, Ks1, Vt1);
+        if (t + 1 < n_tiles) step(t + 1, Ks1, Vt1, Ks0, Vt0);
     }
 
     if (qrow < p.qL) {
