@@ -172,12 +172,30 @@ def summarize(prof_dir, w, commands):
         f"| WRITE_SIZE | {w_raw:.4g} | {write:.4g} |",
         f"| total | | {fetch + write:.4g} ({(fetch + write) / alg:.2f}x algorithmic) |",
         "",
+        f"At the timed average: algorithmic {alg / (timed_us * 1e-6) / 1e9:.0f} GB/s, measured "
+        f"{(fetch + write) / (timed_us * 1e-6) / 1e9:.0f} GB/s, of {PEAK_HBM_GBS:.0f} GB/s HBM peak "
+        f"(roofline bound: {roofline_bound(w)}).",
+        "",
         f"Kernel source sha256 {rec['source_sha256'][:16]}...; bench.py reports this traffic only while it matches.",
         "",
     ]
     with open(os.path.join(PROFILES, f"{w.name}.md"), "w") as f:
         f.write("\n".join(lines))
     log(f"wrote profiles/{w.name}.md and .traffic.json")
+
+
+def find_workload(W, name):
+    every = {x.name: x for x in (*W.CONFIGS.values(), *W.SHORT_KL, *W.RAGGED)}
+    if name not in every:
+        raise SystemExit(f"unknown workload {name!r}; known: {', '.join(sorted(every))}")
+    return every[name]
+
+
+def roofline_bound(w) -> str:
+    """'mfma' when the algorithmic flop per byte is above the ridge of the
+    dtype's matrix peak and the HBM peak, 'hbm' below it."""
+    ridge = PEAK_TFLOPS[w.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    return "mfma" if w.flops() / algorithmic_bytes(w) >= ridge else "hbm"
 
 
 def algorithmic_bytes(w) -> int:
@@ -256,7 +274,7 @@ def main():
     import workloads as W
 
     if args.summarize:
-        w = W.CONFIGS.get(args.workload) or {x.name: x for x in W.RAGGED}[args.workload]
+        w = find_workload(W, args.workload)
         base = f"--workload {w.name}" if w.name != "causal_bf16_d128_8k" else ""
         cmds = {
             "copy_mib": 1024,
@@ -289,7 +307,7 @@ def main():
         log(f"copied {n} bytes device-to-device 3 times")
         return
 
-    w = W.CONFIGS.get(args.workload) or {x.name: x for x in W.RAGGED}[args.workload]
+    w = find_workload(W, args.workload)
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
     log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
@@ -342,8 +360,19 @@ def main():
         cpu = cpu_baseline(w, q, k, v, mask, args.cpu_seconds)
         log(f"cpu baseline: {cpu}")
 
+    bound = roofline_bound(w)
+    gbs = nbytes / (kern_avg_ms * 1e-3) / 1e9
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    roof.update({"traffic": recorded_traffic(w), "kernel_avg_us": round(kern_avg_ms * 1e3, 2)})
+    metric = ("attention fwd TFLOP/s + % MFMA peak, bf16 D=128 causal qL=kL=8192" if w is W.HEADLINE
+              else f"attention fwd TFLOP/s, {w.name}")
     res = {
-        "metric": "attention fwd TFLOP/s + % MFMA peak, bf16 D=128 causal qL=kL=8192",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -360,9 +389,7 @@ def main():
                    "o_layout": "token-major" if w.token_major_out else "head-major",
                    "flop_per_step": flops},
         "mfma_peak_frac": round(achieved / peak, 4),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": recorded_traffic(w),
-                     "kernel_avg_us": round(kern_avg_ms * 1e3, 2)},
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

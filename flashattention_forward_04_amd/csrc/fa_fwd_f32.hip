@@ -333,14 +333,28 @@ hipError_t launch_f32(const FwdParams& p, hipStream_t st)
     FA_F32_VARIANT(D, MASK_BOOL, false, NW, BN, "fwd_f32_d" #D "_bool"),                \
     FA_F32_VARIANT(D, MASK_BOOL, true, NW, BN, "fwd_f32_d" #D "_bool_causal")
 
+// Launch shapes per head dimension (waves per work-group, keys per tile);
+// overridable at build time for tuning sweeps.
+#ifndef FA_F32_D64_CFG
+#define FA_F32_D64_CFG 4, 32
+#endif
+#ifndef FA_F32_D128_CFG
+#define FA_F32_D128_CFG 4, 64
+#endif
+#ifndef FA_F32_D256_CFG
+#define FA_F32_D256_CFG 4, 32
+#endif
+// expands a CFG macro into separate arguments before FA_F32_FOR_D sees them
+#define FA_F32_FOR_D_CFG(D, ...) FA_F32_FOR_D(D, __VA_ARGS__)
+
 // Host-only accessor: a namespace-scope const table would also be emitted
 // for the device, where the launch functions do not exist.
 const Variant* variants_f32(int* n)
 {
     static const Variant table[] = {
-    FA_F32_FOR_D(64, 4, 32),
-    FA_F32_FOR_D(128, 4, 32),
-    FA_F32_FOR_D(256, 4, 32),
+    FA_F32_FOR_D_CFG(64, FA_F32_D64_CFG),
+    FA_F32_FOR_D_CFG(128, FA_F32_D128_CFG),
+    FA_F32_FOR_D_CFG(256, FA_F32_D256_CFG),
 };
     *n = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -72,6 +72,18 @@ def test_config_full_size_sampled(w, n_rows):
         assert np.array_equal(buf, np.transpose(O, (0, 2, 1, 3)).reshape(w.B, w.qL, w.Hq * w.D))
 
 
+@pytest.mark.parametrize("w", W.SHORT_KL, ids=lambda w: w.name)
+def test_short_key_shapes(w):
+    """The HBM-bound short-key shapes at full size (the launch the benchmark
+    times for them); oracle on sampled rows, every row finite."""
+    q, k, v, mask = _draw(w)
+    O, L, _ = run_gpu(q, k, v, mask, causal=w.causal, scale=w.scale)
+    rows = W.sample_rows(w, 1024)
+    Oref, Lref = run_oracle(q, k, v, mask, causal=w.causal, scale=w.scale, rows=rows)
+    assert_parity(O.reshape(-1, w.D)[rows], L.reshape(-1)[rows], Oref, Lref, w.dtype, w.name + " sampled")
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+
+
 # ---------------------------------------------------------------- edge cases
 
 

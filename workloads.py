@@ -68,6 +68,15 @@ C5 = Workload("masked_bf16_d256", "bf16", 1, 8, 8, 1024, 3072, 256, 1 / math.sqr
 CONFIGS = {w.name: w for w in (C1, C2, C3, C4, C5)}
 HEADLINE = C3
 
+# Short-key shapes whose cost is the HBM traffic of Q and O (flop per byte
+# about kL, below the bf16 matrix ridge of ~315): the achieved HBM GB/s is
+# their figure of merit.
+SHORT_KL = [
+    Workload(f"short_kl{kl}_bf16_d128", "bf16", 1, 32, 8, 8192, kl, 128, 1 / math.sqrt(128), seed=20 + kl,
+             note=f"short-key bf16, kL={kl}: HBM-bound (Q and O dominate the bytes)")
+    for kl in (32, 64, 128)
+]
+
 # Ragged shapes that are not tile multiples (the configs above all are).
 RAGGED = [
     Workload("ragged_masked_d256", "bf16", 1, 2, 2, 1000, 3000, 256, 1 / 16, mask_kind="additive",
