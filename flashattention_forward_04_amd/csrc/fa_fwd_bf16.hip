@@ -999,6 +999,9 @@ fwd_bf16_split_kernel(const FwdParams p)
 // Launch: the work-group kernel, or for wide rows whose grid would not give
 // every CU a work-group, the key-split kernel
 // (D = 256 only: narrower rows leave room for more waves per SIMD instead.)
+// At D = 128, key ranges up to kShortKeys take a work-group shape suited to
+// HBM-bound launches.
+constexpr int kShortKeys = 256;
 template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB>
 hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
 {
@@ -1010,6 +1013,17 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
             const dim3 grid((unsigned)q.n_qtiles * q.Hq * q.B);
             hipLaunchKernelGGL((fwd_bf16_split_kernel<D, MASK, CAUSAL, 4, 32>), grid, dim3(4 * 64), 0, st, q);
             return hipGetLastError();
+        }
+    }
+    if constexpr (D == 128) {
+        // Short key ranges are HBM-bound (Q in, O out): 4-wave work-groups
+        // with 32-key tiles keep two work-groups per CU resident, so one's
+        // loads overlap the other's stores (kL = 32: 49 -> 38 us for
+        // 32 heads x 8192 rows); long ones keep the 8-wave shape.
+        if (p.kL <= kShortKeys) {
+            FwdParams q = p;
+            q.n_qtiles = (p.qL + 127) / 128;
+            return launch_bf16<D, MASK, CAUSAL, 4, 32, 2, 0, 2>(q, st);
         }
     }
     return launch_bf16<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB>(p, st);

@@ -165,6 +165,28 @@ def test_wide_rows_work_group_path(causal):
     assert_parity(O.reshape(-1, 256)[rows], L.reshape(-1)[rows], Oref, Lref, "bf16", w.name + " sampled")
 
 
+@pytest.mark.parametrize("kind", ["none", "additive", "bool"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_long_keys_d128(kind, causal):
+    """D = 128 bf16 with more keys than the short-key shape takes (kL > 256):
+    the 8-wave work-group path, ragged in both lengths, every mask kind."""
+    qL, kL = 300, 700
+    q, k, v = _rand((2, 4, qL, 128), BF16, 31), _rand((2, 2, kL, 128), BF16, 32), _rand((2, 2, kL, 128), BF16, 33)
+    mask = None
+    if kind != "none":
+        rng = np.random.default_rng(34)
+        masked = W.draw_masked(rng, (2, 4, qL, kL), 0.3)
+        if kind == "bool":
+            mask = torch.from_numpy((~masked).astype(np.uint8))
+        else:
+            m = rng.standard_normal(masked.shape).astype(np.float32)
+            m[masked] = -np.inf
+            mask = torch.from_numpy(m).to(BF16)
+    O, L, _ = run_gpu(q, k, v, mask, causal=causal, scale=1 / math.sqrt(128))
+    Oref, Lref = run_oracle(q, k, v, mask, causal=causal, scale=1 / math.sqrt(128))
+    assert_parity(O, L, Oref, Lref, "bf16", f"D=128 kL=700 {kind} causal={causal}")
+
+
 def test_bool_mask_equals_additive():
     q, k, v = _rand((1, 2, 64, 128), BF16, 8), _rand((1, 2, 96, 128), BF16, 9), _rand((1, 2, 96, 128), BF16, 10)
     attend = torch.from_numpy(np.random.default_rng(11).random((1, 2, 64, 96)) < 0.5)
