@@ -257,38 +257,67 @@ fwd_bf16_kernel(const FwdParams p)
     // (the hardware places lane l's 16 bytes at the block base + 16 l).  A
     // slot in a row's pad is skipped; rows past kL load row kL - 1 (finite
     // values; their scores are masked, so they only meet P = 0).
-    auto issue_tile = [&](const uint16_t* gbase, int64_t stride, int j0, uint16_t* lds, auto spr_c, auto nins_c)
-        __attribute__((always_inline)) {
+    // A lane's slots are the same in every tile: their element offsets
+    // within a tile (row * stride + chunk * 8) are computed once, so a full
+    // tile's load address is one add; only the tail tile (rows past kL,
+    // clamped) recomputes them.
+    constexpr int KIT = (KINS + NW - 1) / NW;  // direct loads per wave per K tile (at most)
+    constexpr int VIT = (VINS + NW - 1) / NW;
+    int64_t koff[KIT], voff[VIT];
+    auto slot_offsets = [&](int64_t* off, int64_t stride, auto spr_c, auto nins_c) __attribute__((always_inline)) {
         constexpr int SPR = decltype(spr_c)::value;
         constexpr int NINS = decltype(nins_c)::value;
 #pragma unroll
         for (int k = 0; k < (NINS + NW - 1) / NW; ++k) {
-            const int i = wave + k * NW;
-            if (NINS % NW != 0 && i >= NINS) break;
-            const int slot = 64 * i + lane;
-            const int row = slot / SPR;
-            const int ch = slot % SPR;
-            if (ch < D / 8 && row < BN) {
-                const int j = min(j0 + row, p.kL - 1);
-                if (MASK == MASK_NONE) {
-                    lds_dma16(gbase + (int64_t)j * stride + ch * 8,
-                              (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(lds + 512 * i));
-                } else {
-                    // the masked kernels load the mask with ordinary loads
-                    // whose compiler waits would also wait for untracked
-                    // direct loads, so here the compiler tracks them
-                    __builtin_amdgcn_global_load_lds(
-                        (__attribute__((address_space(1))) void*)(gbase + (int64_t)j * stride + ch * 8),
-                        (__attribute__((address_space(3))) void*)(lds + 512 * i), 16, 0, 0);
-                }
-            }
+            const int slot = 64 * (wave + k * NW) + lane;
+            off[k] = (int64_t)(slot / SPR) * stride + (slot % SPR) * 8;
         }
     };
+    slot_offsets(koff, p.k_s[2], std::integral_constant<int, KSPR>{}, std::integral_constant<int, KINS>{});
+    slot_offsets(voff, p.v_s[2], std::integral_constant<int, VSPR>{}, std::integral_constant<int, VINS>{});
+    auto issue_tile = [&](const uint16_t* gbase, int64_t stride, int j0, uint16_t* lds, const int64_t* off,
+                          auto spr_c, auto nins_c) __attribute__((always_inline)) {
+        constexpr int SPR = decltype(spr_c)::value;
+        constexpr int NINS = decltype(nins_c)::value;
+        auto all_slots = [&](auto full_c) __attribute__((always_inline)) {
+            constexpr bool FULL = decltype(full_c)::value;
+            const uint16_t* tbase = gbase + (int64_t)j0 * stride;
+#pragma unroll
+            for (int k = 0; k < (NINS + NW - 1) / NW; ++k) {
+                const int i = wave + k * NW;
+                if (NINS % NW != 0 && i >= NINS) break;
+                const int slot = 64 * i + lane;
+                const int row = slot / SPR;
+                const int ch = slot % SPR;
+                if (ch < D / 8 && row < BN) {
+                    const uint16_t* src =
+                        FULL ? tbase + off[k] : gbase + (int64_t)min(j0 + row, p.kL - 1) * stride + ch * 8;
+                    if (MASK == MASK_NONE) {
+                        lds_dma16(src, (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(lds + 512 * i));
+                    } else {
+                        // the masked kernels load the mask with ordinary
+                        // loads whose compiler waits would also wait for
+                        // untracked direct loads, so here the compiler
+                        // tracks them
+                        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                                         (__attribute__((address_space(3))) void*)(lds + 512 * i), 16,
+                                                         0, 0);
+                    }
+                }
+            }
+        };
+        if (j0 + BN <= p.kL)
+            all_slots(std::true_type{});
+        else
+            all_slots(std::false_type{});
+    };
     auto issue_k = [&](int t, uint16_t* kt) __attribute__((always_inline)) {
-        issue_tile(Kb, p.k_s[2], t * BN, kt, std::integral_constant<int, KSPR>{}, std::integral_constant<int, KINS>{});
+        issue_tile(Kb, p.k_s[2], t * BN, kt, koff, std::integral_constant<int, KSPR>{},
+                   std::integral_constant<int, KINS>{});
     };
     auto issue_v = [&](int t, uint16_t* vt) __attribute__((always_inline)) {
-        issue_tile(Vb, p.v_s[2], t * BN, vt, std::integral_constant<int, VSPR>{}, std::integral_constant<int, VINS>{});
+        issue_tile(Vb, p.v_s[2], t * BN, vt, voff, std::integral_constant<int, VSPR>{},
+                   std::integral_constant<int, VINS>{});
     };
     // all of this wave's direct loads have landed in LDS
     auto wait_loads = []() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0x0F70); };
