@@ -28,6 +28,7 @@ struct FwdParams {
     float scale_log2;   // |scale| * log2(e): scores live in base 2
     int neg_q;          // scale < 0: Q's sign bit is flipped on load instead
     int mask_vec;       // mask rows admit 4-element vector loads
+    int pair_tiles;     // causal: the whole grid is resident at once (see causal_tile)
 };
 
 enum MaskKind { MASK_NONE = 0, MASK_ADD = 1, MASK_BOOL = 2 };
@@ -40,6 +41,26 @@ enum MaskKind { MASK_NONE = 0, MASK_ADD = 1, MASK_BOOL = 2 };
 // from its own L2.  Other head counts keep the plain order.
 __device__ __forceinline__ int head_of(int slot, int Hq) {
     return (Hq % 8 == 0) ? (slot % 8) * (Hq / 8) + slot / 8 : slot;
+}
+
+// Causal query tiles differ in length (tile t sees t + 1 key blocks).
+// Work-group rank r (ids in dispatch order, one rank per H_q * B ids) gets
+// tile n - 1 - r, longest first, which balances a grid that runs in several
+// rounds.  When the whole grid is resident at once the second half is
+// reversed (shortest first), so that the work-groups placed second on each
+// CU complement the first: rank r and rank r + (n + 1) / 2 get tiles n - 1 - r
+// and r, n + 1 key blocks together.
+__device__ __forceinline__ int causal_tile(int rank, int n, int pair) {
+    if (!pair) return n - 1 - rank;
+    const int half = (n + 1) / 2;
+    return rank < half ? n - 1 - rank : rank - half;
+}
+
+// True when a grid of `wgs` work-groups fits on the GPU at once, given how
+// many work-groups one CU holds.
+inline bool grid_fits_at_once(int64_t wgs, int wgs_per_cu) {
+    constexpr int kCUs = 256;
+    return wgs <= (int64_t)kCUs * (wgs_per_cu > 0 ? wgs_per_cu : 1);
 }
 
 // One direct global -> LDS load (global_load_lds_dwordx4): lane l's 16

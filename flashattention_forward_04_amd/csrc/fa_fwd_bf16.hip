@@ -206,7 +206,7 @@ fwd_bf16_kernel(const FwdParams p)
     id /= p.Hq;
     const int b = id % p.B;
     id /= p.B;
-    const int qt = CAUSAL ? (p.n_qtiles - 1 - id) : id;  // longest causal tiles first
+    const int qt = CAUSAL ? causal_tile(id, p.n_qtiles, p.pair_tiles) : id;
     const int q0 = qt * BM;
     const int hk = h / p.group;
     const int wq0 = q0 + wave * 32;  // first query row of this wave
@@ -707,8 +707,15 @@ fwd_bf16_kernel(const FwdParams p)
 template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB>
 hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
 {
-    const dim3 grid((unsigned)p.n_qtiles * p.Hq * p.B);
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB>), grid, dim3(NW * 64), 0, st, p);
+    // work-groups one CU holds: by waves per SIMD, and by LDS (tiles padded
+    // to 1 KiB blocks, NB buffers each for K and V)
+    constexpr int kLdsPerWg = NB * ((BN * (D + 8) / 8 + 63) / 64 + (BN * (D + 32) / 8 + 63) / 64) * 1024;
+    constexpr int kWgsPerCu = (4 * WPE / NW < 160 * 1024 / kLdsPerWg) ? 4 * WPE / NW : 160 * 1024 / kLdsPerWg;
+    FwdParams q = p;
+    const int64_t wgs = (int64_t)p.n_qtiles * p.Hq * p.B;
+    q.pair_tiles = CAUSAL && grid_fits_at_once(wgs, kWgsPerCu);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB>), dim3((unsigned)wgs), dim3(NW * 64),
+                       0, st, q);
     return hipGetLastError();
 }
 
@@ -764,7 +771,7 @@ fwd_bf16_split_kernel(const FwdParams p)
     id /= p.Hq;
     const int b = id % p.B;
     id /= p.B;
-    const int qt = CAUSAL ? (p.n_qtiles - 1 - id) : id;
+    const int qt = CAUSAL ? causal_tile(id, p.n_qtiles, p.pair_tiles) : id;
     const int q0 = qt * 32;
     const int qrow = q0 + r32;
     const int hk = h / p.group;
@@ -1039,6 +1046,7 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
         if ((int64_t)p.n_qtiles * p.Hq * p.B < kCUs) {
             FwdParams q = p;
             q.n_qtiles = (p.qL + 31) / 32;
+            q.pair_tiles = CAUSAL && grid_fits_at_once((int64_t)q.n_qtiles * q.Hq * q.B, 1);
             const dim3 grid((unsigned)q.n_qtiles * q.Hq * q.B);
             hipLaunchKernelGGL((fwd_bf16_split_kernel<D, MASK, CAUSAL, 4, 32>), grid, dim3(4 * 64), 0, st, q);
             return hipGetLastError();

@@ -70,7 +70,7 @@ fwd_f32_kernel(const FwdParams p)
     id /= p.Hq;
     const int b = id % p.B;
     id /= p.B;
-    const int qt = CAUSAL ? (p.n_qtiles - 1 - id) : id;
+    const int qt = CAUSAL ? causal_tile(id, p.n_qtiles, p.pair_tiles) : id;
     const int q0 = qt * BM;
     const int hk = h / p.group;
     const int wq0 = q0 + wave * 32;
@@ -315,8 +315,10 @@ fwd_f32_kernel(const FwdParams p)
 template <int D, int MASK, bool CAUSAL, int NW, int BN>
 hipError_t launch_f32(const FwdParams& p, hipStream_t st)
 {
-    const dim3 grid((unsigned)p.n_qtiles * p.Hq * p.B);
-    hipLaunchKernelGGL((fwd_f32_kernel<D, MASK, CAUSAL, NW, BN>), grid, dim3(NW * 64), 0, st, p);
+    FwdParams q = p;
+    const int64_t wgs = (int64_t)p.n_qtiles * p.Hq * p.B;
+    q.pair_tiles = CAUSAL && grid_fits_at_once(wgs, 1);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, MASK, CAUSAL, NW, BN>), dim3((unsigned)wgs), dim3(NW * 64), 0, st, q);
     return hipGetLastError();
 }
 
