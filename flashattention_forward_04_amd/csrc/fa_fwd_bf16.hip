@@ -1032,6 +1032,199 @@ fwd_bf16_split_kernel(const FwdParams p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming forward for short key ranges (kL <= 32 NT).  The cost of such a
+// launch is reading Q and writing O once (flop per byte about kL, below the
+// matrix ridge), so the kernel is built to keep HBM busy:
+//   * a work-group stays on one kv head, loads all of its K and V into LDS
+//     once (at most NT tiles of 32 keys), and then needs no barrier;
+//   * each wave walks a strided list of 32-row query blocks of that head's
+//     query-head group; the next block's Q is loaded into registers while
+//     the current block is computed and its O stored (the raw words are
+//     converted only where they are used, so nothing waits for them early);
+//   * the grid is sized to the number of work-groups the GPU holds at once.
+template <int D, bool CAUSAL, int NW, int NT>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_bf16_stream_kernel(const FwdParams p, int wgs_per_head)
+{
+    constexpr int BN = 32;
+    using KL = TileLayout<D + 8>;
+    using VL = TileLayout<D + 32>;
+    constexpr int KSPR = KL::PITCH / 8, VSPR = VL::PITCH / 8;
+    constexpr int KINS = (BN * KSPR + 63) / 64, VINS = (BN * VSPR + 63) / 64;
+    constexpr int KTILE = KINS * 512, VTILE = VINS * 512;
+    constexpr int DK = D / 16, ND = D / 32;
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks[NT * KTILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs[NT * VTILE];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r32 = lane & 31, g = lane >> 5, lt = lane & 15;
+
+    // work-group -> (batch, kv head, slot among the head's work-groups)
+    const int slot = blockIdx.x % wgs_per_head;
+    const int bh = blockIdx.x / wgs_per_head;
+    const int hk = bh % p.Hkv;
+    const int b = bh / p.Hkv;
+    const uint16_t* Kb = (const uint16_t*)p.k + b * p.k_s[0] + hk * p.k_s[1];
+    const uint16_t* Vb = (const uint16_t*)p.v + b * p.v_s[0] + hk * p.v_s[1];
+    const int n_tiles = (p.kL + BN - 1) / BN;  // <= NT
+
+    // ---- all K and V tiles of this head into LDS (rows past kL repeat row kL - 1) ----
+    auto load_tile = [&](const uint16_t* gbase, int64_t stride, uint16_t* lds, auto spr_c, auto nins_c, int t)
+        __attribute__((always_inline)) {
+        constexpr int SPR = decltype(spr_c)::value;
+        constexpr int NINS = decltype(nins_c)::value;
+        for (int i = wave; i < NINS; i += NW) {
+            const int sl = 64 * i + lane;
+            const int row = sl / SPR, ch = sl % SPR;
+            if (ch < D / 8 && row < BN) {
+                const int j = min(t * BN + row, p.kL - 1);
+                lds_dma16(gbase + (int64_t)j * stride + ch * 8,
+                          (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(lds + 512 * i));
+            }
+        }
+    };
+    for (int t = 0; t < n_tiles; ++t) {
+        load_tile(Kb, p.k_s[2], Ks + t * KTILE, std::integral_constant<int, KSPR>{},
+                  std::integral_constant<int, KINS>{}, t);
+        load_tile(Vb, p.v_s[2], Vs + t * VTILE, std::integral_constant<int, VSPR>{},
+                  std::integral_constant<int, VINS>{}, t);
+    }
+
+    // ---- this wave's query blocks: block q of the group's group * nqb ----
+    const int nqb = (p.qL + 31) / 32;
+    const int nblk = p.group * nqb;
+    const int stride_blk = wgs_per_head * NW;
+    const float c2 = p.scale_log2;
+    const uint32_t flip = p.neg_q ? 0x80008000u : 0u;
+
+    // raw Q words of a block; the sign flip and the zeroing of rows past qL
+    // are applied where the block is computed, so nothing waits for these
+    // loads before then.  Always DK loads (from an in-range row), so the
+    // number of loads in flight is known when waiting below.
+    auto q_load = [&](int blk, u32x4 (&qw)[DK]) __attribute__((always_inline)) {
+        const int bc = min(blk, nblk - 1);
+        const int h = hk * p.group + bc / nqb;
+        const int qrow = min((bc % nqb) * 32 + r32, p.qL - 1);
+        const u32x4* src =
+            (const u32x4*)((const uint16_t*)p.q + b * p.q_s[0] + h * p.q_s[1] + (int64_t)qrow * p.q_s[2]);
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) qw[ks] = src[2 * ks + g];
+    };
+
+    auto block = [&](int blk, const u32x4 (&qw)[DK]) __attribute__((always_inline)) {
+        const int h = hk * p.group + blk / nqb;
+        const int q0 = (blk % nqb) * 32;
+        const int qrow = q0 + r32;
+        bf16x8 qf[DK];
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks)
+            qf[ks] = __builtin_bit_cast(bf16x8, qrow < p.qL ? (qw[ks] ^ flip) : u32x4{0, 0, 0, 0});
+        f32x16 o[ND];
+#pragma unroll
+        for (int d = 0; d < ND; ++d) o[d] = f32x16{};
+        float m_run = -INFINITY, l_run = 0.f;
+        const int t_end = CAUSAL ? min(n_tiles, (q0 + 31) / BN + 1) : n_tiles;
+        for (int t = 0; t < t_end; ++t) {
+            const uint16_t* kt = Ks + t * KTILE;
+            const uint16_t* vt = Vs + t * VTILE;
+            const int j0 = t * BN;
+            f32x16 s = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < DK; ++ks) {
+                const bf16x8 kop = *(const bf16x8*)(kt + KL::off(r32, 2 * ks + g));
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[ks], s, 0, 0, 0);
+            }
+            const bool masked = (j0 + BN > p.kL) || (CAUSAL && j0 + BN - 1 > q0);
+            if (masked) {
+                int lim = p.kL - 1;
+                if (CAUSAL) lim = min(lim, qrow);
+                lim -= j0 + 4 * g;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3) <= lim) ? s[r] * c2 : -INFINITY;
+            }
+            const float cs = masked ? 1.f : c2;
+            float mx = s[0];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+            const float m_tile = row_max_halves(mx) * cs;
+            if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
+                const float m_new = fmaxf(m_run, m_tile);
+                if (m_run != -INFINITY && m_new != m_run) {
+                    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+                    l_run *= corr;
+#pragma unroll
+                    for (int d = 0; d < ND; ++d) o[d] *= corr;
+                }
+                m_run = m_new;
+            }
+            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+            float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                u32x4 pw;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * hh + 2 * e], cs, -m_use));
+                    const float z = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * hh + 2 * e + 1], cs, -m_use));
+                    pw[e] = pack_bf16x2(a, z);
+                    rs0 += a;
+                    rs1 += z;
+                }
+                const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+                for (int d = 0; d < ND; ++d) {
+                    const int col = 32 * d + 16 * ((lane >> 4) & 1) + 4 * (lt & 3);
+                    const int row0 = 16 * hh + 4 * g + (lt >> 2);
+                    const i16x4 v0 = lds_read_tr(vt + VL::off(row0, 0) + col);
+                    const i16x4 v1 = lds_read_tr(vt + VL::off(row0 + 8, 0) + col);
+                    const bf16x8 vop =
+                        __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+                    o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pf, o[d], 0, 0, 0);
+                }
+            }
+            l_run += row_sum_halves(rs0 + rs1);
+        }
+        if (qrow < p.qL) {
+            const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
+            uint16_t* orow = (uint16_t*)p.o + b * p.o_s[0] + h * p.o_s[1] + (int64_t)qrow * p.o_s[2];
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    u32x2 w;
+                    w[0] = pack_bf16x2(o[d][4 * rq + 0] * inv, o[d][4 * rq + 1] * inv);
+                    w[1] = pack_bf16x2(o[d][4 * rq + 2] * inv, o[d][4 * rq + 3] * inv);
+                    *(u32x2*)(orow + 32 * d + 8 * rq + 4 * g) = w;
+                }
+            if (g == 0) {
+                const float lse = (l_run > 0.f) ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : 0.f;
+                p.lse[((int64_t)b * p.Hq + h) * p.qL + qrow] = lse;
+            }
+        }
+    };
+
+    // two Q buffers, unrolled by two: the next block's Q is in flight while
+    // a block computes and stores (the first is issued before waiting for
+    // the K/V staging)
+    u32x4 qa[DK], qb[DK];
+    int blk = slot * NW + wave;
+    q_load(blk, qa);
+    // K and V in LDS; the DK loads of the first Q block, issued after them,
+    // may still be in flight
+    static_assert(DK < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (DK & 15) | ((DK >> 4) << 14));
+    __syncthreads();
+    for (; blk < nblk; blk += 2 * stride_blk) {
+        q_load(blk + stride_blk, qb);
+        block(blk, qa);
+        if (blk + stride_blk >= nblk) break;
+        q_load(blk + 2 * stride_blk, qa);
+        block(blk + stride_blk, qb);
+    }
+}
+
 // Launch: the work-group kernel, or for wide rows whose grid would not give
 // every CU a work-group, the key-split kernel
 // (D = 256 only: narrower rows leave room for more waves per SIMD instead.)
@@ -1057,6 +1250,18 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
         // with 32-key tiles keep two work-groups per CU resident, so one's
         // loads overlap the other's stores (kL = 32: 49 -> 38 us for
         // 32 heads x 8192 rows); long ones keep the 8-wave shape.
+        if (MASK == MASK_NONE && p.kL <= 4 * 32) {
+            // streaming kernel: enough work-groups per kv head to fill the
+            // GPU twice over, each with at least a few query blocks per wave
+            constexpr int kResident = 2 * 256;
+            const int heads = p.B * p.Hkv;
+            const int blocks = p.group * ((p.qL + 31) / 32);
+            int per_head = (kResident + heads - 1) / heads;
+            per_head = max(1, min(per_head, blocks / 4));
+            const dim3 grid((unsigned)(per_head * heads));
+            hipLaunchKernelGGL((fwd_bf16_stream_kernel<D, CAUSAL, 4, 4>), grid, dim3(4 * 64), 0, st, p, per_head);
+            return hipGetLastError();
+        }
         if (p.kL <= kShortKeys) {
             FwdParams q = p;
             q.n_qtiles = (p.qL + 127) / 128;

@@ -187,6 +187,17 @@ def test_long_keys_d128(kind, causal):
     assert_parity(O, L, Oref, Lref, "bf16", f"D=128 kL=700 {kind} causal={causal}")
 
 
+@pytest.mark.parametrize("qL,kL,causal", [(300, 100, True), (300, 100, False), (97, 33, True), (64, 128, False),
+                                          (1, 7, False), (200, 1, True)])
+def test_short_keys_streaming(qL, kL, causal):
+    """D = 128 bf16 unmasked with kL <= 128: the streaming kernel (K/V held
+    in LDS, query blocks walked per wave), GQA group of 4, ragged lengths."""
+    q, k, v = _rand((2, 8, qL, 128), BF16, 41), _rand((2, 2, kL, 128), BF16, 42), _rand((2, 2, kL, 128), BF16, 43)
+    O, L, _ = run_gpu(q, k, v, None, causal=causal, scale=1 / math.sqrt(128))
+    Oref, Lref = run_oracle(q, k, v, None, causal=causal, scale=1 / math.sqrt(128))
+    assert_parity(O, L, Oref, Lref, "bf16", f"streaming qL={qL} kL={kL} causal={causal}")
+
+
 def test_bool_mask_equals_additive():
     q, k, v = _rand((1, 2, 64, 128), BF16, 8), _rand((1, 2, 96, 128), BF16, 9), _rand((1, 2, 96, 128), BF16, 10)
     attend = torch.from_numpy(np.random.default_rng(11).random((1, 2, 64, 96)) < 0.5)
