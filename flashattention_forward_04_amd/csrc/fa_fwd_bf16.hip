@@ -146,6 +146,7 @@ template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int 
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fwd_bf16_kernel(const FwdParams p)
 {
+    static_assert(SCHED == 0 || SCHED == 1, "schedule: 0 plain, 1 pipelined");
     constexpr bool PIPE = SCHED != 0;  // next tile's scores formed during this tile's softmax
     constexpr int BM = NW * 32;       // query rows per work-group
     using KL = TileLayout<D + 8>;     // K tile layout in LDS
@@ -435,19 +436,11 @@ fwd_bf16_kernel(const FwdParams p)
     //             K operands of group r+2.
     // Stages are fenced (sched_barrier), and inside a stage the products and
     // vector instructions are issued alternately (sched_group_barrier).
-    //
-    // ORD says where the next tile's score products go: 0 nowhere (not
-    // pipelined), 1 spread over the stages as above, 2 all in stage -1, 3 all
-    // after the last P V.  Orders 2 and 3 run on the two halves of the waves
-    // (ping-pong): the two waves sharing a SIMD then issue their products at
-    // different times, and one wave's vector work runs beside the other's
-    // products.
-    auto softmax_pv = [&](f32x16 (&s)[NC], float cs, const uint16_t* vt, f32x16 (&sn)[NC], const uint16_t* kn,
-                          auto ord_c) __attribute__((always_inline)) {
-        constexpr int ORD = decltype(ord_c)::value;
-        constexpr int NCH = 2 * NC;                                // 16-key blocks per tile
-        constexpr int NS = (ORD == 1) ? NP : 0;                    // products spread over the stages
-        constexpr int SS = (ORD == 1) ? (NP + NCH) / (NCH + 1) : 0;  // products per group
+    auto softmax_pv = [&](f32x16 (&s)[NC], float cs, const uint16_t* vt, f32x16 (&sn)[NC], const uint16_t* kn)
+        __attribute__((always_inline)) {
+        constexpr int NCH = 2 * NC;                            // 16-key blocks per tile
+        constexpr int NS = PIPE ? NP : 0;                      // next-tile score products
+        constexpr int SS = PIPE ? (NP + NCH) / (NCH + 1) : 0;  // products per group
         constexpr int SSB = SS > 0 ? SS : 1;
         bf16x8 kb[2][SSB];  // K operands, by group parity
         bf16x8 vb[2][ND];   // V^T operands, by block parity
@@ -490,30 +483,6 @@ fwd_bf16_kernel(const FwdParams p)
                 o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[kidx & 1][d], pf[kidx & 1], o[d], 0, 0, 0);
         };
 
-        // all NP score products of the next tile, reading their K operands as
-        // they go (orders 2 and 3)
-        auto s_block = [&]() __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < NP; ++i) {
-                const int ks = i / NC, c = i % NC;
-                const bf16x8 kop = *(const bf16x8*)(kn + KL::off(32 * c + r32, 2 * ks + g));
-                sn[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[ks], ks == 0 ? f32x16{} : sn[c], 0, 0, 0);
-            }
-            // keep four operand reads in flight ahead of the products
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
-#pragma unroll
-            for (int i = 0; i < NP - 4; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 2);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 2);
-        };
-
-        if (ORD == 2) {
-            s_block();
-            __builtin_amdgcn_sched_barrier(0);
-        }
         // stage -1: group 0's operands are needed at once (their latency is
         // covered by the row max); group 1's are read behind the first product
         k_read(0);
@@ -525,7 +494,7 @@ fwd_bf16_kernel(const FwdParams p)
         const float m_tile = row_max_halves(mx) * cs;
         s_mma(0);
         k_read(1);
-        if (ORD == 1) {
+        if (PIPE) {
             __builtin_amdgcn_sched_group_barrier(0x100, SS, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -584,10 +553,6 @@ fwd_bf16_kernel(const FwdParams p)
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (ORD == 3) {
-            s_block();
-            __builtin_amdgcn_sched_barrier(0);
-        }
         l_run += row_sum_halves(rs0 + rs1);
     };
 
@@ -601,15 +566,7 @@ fwd_bf16_kernel(const FwdParams p)
         // softmax would make the register allocator move them at the join)
         if (masked) apply_mask(s, j0, mw);
         const float cs = masked ? 1.f : c2;
-        if (SCHED == 0) {
-            softmax_pv(s, cs, vt, sn, kn, std::integral_constant<int, 0>{});
-        } else if (SCHED == 1) {
-            softmax_pv(s, cs, vt, sn, kn, std::integral_constant<int, 1>{});
-        } else if (2 * wave < NW) {
-            softmax_pv(s, cs, vt, sn, kn, std::integral_constant<int, 2>{});
-        } else {
-            softmax_pv(s, cs, vt, sn, kn, std::integral_constant<int, 3>{});
-        }
+        softmax_pv(s, cs, vt, sn, kn);
     };
 
     f32x16 sa[NC], sb[NC];  // score tiles (two, for the pipelined schedule)
