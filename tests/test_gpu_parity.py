@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import flashattention_forward_04_amd as fa
 import workloads as W
 from gpu_util import TOL_L, TOL_O, assert_parity, dtype_name, max_err, run_gpu, run_oracle
 
@@ -313,3 +314,46 @@ def test_repeat_calls_are_deterministic():
     O1, L1, _ = run_gpu(q, k, v, causal=True, scale=w.scale)
     O2, L2, _ = run_gpu(q, k, v, causal=True, scale=w.scale)
     assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+@pytest.mark.parametrize("kL,causal", [(64, False), (320, True)], ids=["stream_kL64", "workgroup_kL320_causal"])
+def test_tensors_past_2pow31_elements(kL, causal):
+    """Maximum sizes: Q and O hold more than 2^31 elements each (byte offsets
+    past 2^32), so every row offset must be computed in 64 bits.  Rows are
+    sampled across the whole range, the very last row included, and checked
+    against the oracle on that row's allowed keys (top-left causal: keys
+    0..i); every row must be finite and inside the range of its head's V."""
+    B, Hq, Hkv, D = 1, 32, 8, 128
+    qL = (1 << 31) // (Hq * D) + 4096
+    scale = 1 / math.sqrt(D)
+    print(f"[case] large B={B} Hq={Hq} Hkv={Hkv} qL={qL} kL={kL} D={D} bf16 causal={causal} seed=31", flush=True)
+    assert B * Hq * qL * D > (1 << 31)
+    dev = torch.device("cuda:0")
+    gq = torch.Generator(device=dev).manual_seed(31)
+    q = torch.randn((B, Hq, qL, D), generator=gq, device=dev, dtype=torch.bfloat16)
+    k = _rand((B, Hkv, kL, D), BF16, 32)
+    v = _rand((B, Hkv, kL, D), BF16, 33)
+    O, L = fa.fwd(q, k.to(dev), v.to(dev), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(O).all()) and bool(torch.isfinite(L).all())
+    grp = Hq // Hkv
+    vmin, vmax = v.float().amin(dim=2), v.float().amax(dim=2)  # [B, Hkv, D]
+    for h in range(Hq):
+        oh = O[0, h].float()
+        lo, hi = vmin[0, h // grp].to(dev), vmax[0, h // grp].to(dev)
+        assert bool((oh >= lo - TOL_O["bf16"]).all()) and bool((oh <= hi + TOL_O["bf16"]).all()), f"head {h}"
+        del oh
+    rng = np.random.default_rng(34)
+    picks = [(0, 0), (Hq - 1, qL - 1), (Hq - 1, qL - 2), (Hq // 2, qL // 2), (0, kL - 1), (0, min(kL, qL - 1))]
+    picks += [(int(rng.integers(Hq)), int(rng.integers(qL))) for _ in range(40)]
+    errs_o, errs_l = [], []
+    for h, i in picks:
+        n = min(i + 1, kL) if causal else kL
+        qi = q[0, h, i].cpu().reshape(1, 1, 1, D)
+        ki, vi = k[:, h // grp: h // grp + 1, :n], v[:, h // grp: h // grp + 1, :n]
+        Oref, Lref = run_oracle(qi, ki, vi, causal=False, scale=scale)
+        errs_o.append(max_err(O[0, h, i].double().cpu().numpy(), Oref.reshape(D)))
+        errs_l.append(abs(float(L[0, h, i]) - float(Lref.reshape(()))))
+    print(f"[parity] large kL={kL}: max|dO| = {max(errs_o):.3e}, max|dL| = {max(errs_l):.3e} over {len(picks)} rows",
+          flush=True)
+    assert max(errs_o) <= TOL_O["bf16"] and max(errs_l) <= TOL_L
