@@ -1233,6 +1233,12 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
 // Launch shapes per head dimension and mask use: waves per work-group, keys
 // per tile, waves per SIMD, pipelined (1) or not (0), LDS ring depth (2 or
 // 4).  Overridable at build time for tuning sweeps.
+#ifndef FA_BF16_D32_CFG
+#define FA_BF16_D32_CFG 4, 64, 2, 1, 2
+#endif
+#ifndef FA_BF16_D32_MASKED_CFG
+#define FA_BF16_D32_MASKED_CFG 4, 64, 2, 0, 2
+#endif
 #ifndef FA_BF16_D64_CFG
 #define FA_BF16_D64_CFG 4, 64, 2, 1, 2
 #endif
@@ -1244,6 +1250,12 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
 #endif
 #ifndef FA_BF16_D128_MASKED_CFG
 #define FA_BF16_D128_MASKED_CFG 8, 64, 2, 0, 2
+#endif
+#ifndef FA_BF16_D96_CFG
+#define FA_BF16_D96_CFG 8, 64, 2, 0, 2
+#endif
+#ifndef FA_BF16_D96_MASKED_CFG
+#define FA_BF16_D96_MASKED_CFG 8, 64, 2, 0, 2
 #endif
 #ifndef FA_BF16_D256_CFG
 #define FA_BF16_D256_CFG 4, 32, 1, 0, 2
@@ -1270,7 +1282,9 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
 const Variant* variants_bf16(int* n)
 {
     static const Variant table[] = {
+    FA_BF16_FOR_D(32, FA_BF16_D32_CFG, FA_BF16_D32_MASKED_CFG),
     FA_BF16_FOR_D(64, FA_BF16_D64_CFG, FA_BF16_D64_MASKED_CFG),
+    FA_BF16_FOR_D(96, FA_BF16_D96_CFG, FA_BF16_D96_MASKED_CFG),
     FA_BF16_FOR_D(128, FA_BF16_D128_CFG, FA_BF16_D128_MASKED_CFG),
     FA_BF16_FOR_D(256, FA_BF16_D256_CFG, FA_BF16_D256_MASKED_CFG),
 };

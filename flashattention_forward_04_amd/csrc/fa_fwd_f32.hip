@@ -337,11 +337,17 @@ hipError_t launch_f32(const FwdParams& p, hipStream_t st)
 
 // Launch shapes per head dimension (waves per work-group, keys per tile);
 // overridable at build time for tuning sweeps.
+#ifndef FA_F32_D32_CFG
+#define FA_F32_D32_CFG 4, 32
+#endif
 #ifndef FA_F32_D64_CFG
 #define FA_F32_D64_CFG 4, 32
 #endif
 #ifndef FA_F32_D128_CFG
 #define FA_F32_D128_CFG 4, 64
+#endif
+#ifndef FA_F32_D96_CFG
+#define FA_F32_D96_CFG 4, 64
 #endif
 #ifndef FA_F32_D256_CFG
 #define FA_F32_D256_CFG 4, 32
@@ -354,7 +360,9 @@ hipError_t launch_f32(const FwdParams& p, hipStream_t st)
 const Variant* variants_f32(int* n)
 {
     static const Variant table[] = {
+    FA_F32_FOR_D_CFG(32, FA_F32_D32_CFG),
     FA_F32_FOR_D_CFG(64, FA_F32_D64_CFG),
+    FA_F32_FOR_D_CFG(96, FA_F32_D96_CFG),
     FA_F32_FOR_D_CFG(128, FA_F32_D128_CFG),
     FA_F32_FOR_D_CFG(256, FA_F32_D256_CFG),
 };

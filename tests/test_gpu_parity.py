@@ -45,7 +45,8 @@ def test_ragged(w):
     _full_parity(w)
 
 
-@pytest.mark.parametrize("w,n_rows", [(W.C3, 1536), (W.C4, 768)], ids=lambda x: getattr(x, "name", str(x)))
+@pytest.mark.parametrize("w,n_rows", [(W.C3, 1536), (W.C4, 768), *[(x, 768) for x in W.HEAD_DIMS]],
+                         ids=lambda x: getattr(x, "name", str(x)))
 def test_config_full_size_sampled(w, n_rows):
     """Full-size launch (the configuration the benchmark times); oracle on sampled rows."""
     q, k, v, mask = _draw(w)
@@ -94,7 +95,7 @@ def _rand(shape, dtype, seed):
 
 
 @pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", [32, 64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 def test_head_dims_and_dtypes(dtype, D, causal):
     q = _rand((1, 4, 200, D), dtype, 1)
@@ -109,8 +110,8 @@ def test_head_dims_and_dtypes(dtype, D, causal):
 @pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("kind", ["additive", "bool"])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
-def test_masks(dtype, kind, causal):
-    D = 64
+@pytest.mark.parametrize("D", [32, 64, 96])
+def test_masks(dtype, kind, causal, D):
     q, k, v = _rand((2, 2, 70, D), dtype, 4), _rand((2, 2, 90, D), dtype, 5), _rand((2, 2, 90, D), dtype, 6)
     rng = np.random.default_rng(7)
     masked = W.draw_masked(rng, (2, 2, 70, 90), 0.3)
@@ -123,7 +124,7 @@ def test_masks(dtype, kind, causal):
         mask = torch.from_numpy(m).to(dtype)
     O, L, _ = run_gpu(q, k, v, mask, causal=causal, scale=0.125)
     Oref, Lref = run_oracle(q, k, v, mask, causal=causal, scale=0.125)
-    assert_parity(O, L, Oref, Lref, dtype_name(q), f"{kind} mask causal={causal}")
+    assert_parity(O, L, Oref, Lref, dtype_name(q), f"{kind} mask causal={causal} D={D}")
     assert np.all(O[0, 1, 5] == 0) and L[0, 1, 5] == 0, "row with no allowed key is not O = 0, L = 0"
 
 
