@@ -112,8 +112,8 @@ fa_status fa_fwd_strided(const void* Q, const void* K, const void* V, const void
     if (H_q % H_kv != 0) return fail(E, "fa_fwd: H_q (%d) must be divisible by H_kv (%d)", H_q, H_kv);
     if (qL <= 0) return fail(E, "fa_fwd: qL must be > 0, got %d", qL);
     if (kL <= 0) return fail(E, "fa_fwd: kL must be > 0, got %d", kL);
-    if (D != 32 && D != 64 && D != 96 && D != 128 && D != 256)
-        return fail(E, "fa_fwd: D must be 32, 64, 96, 128 or 256, got %d", D);
+    if (D != 16 && D != 32 && D != 48 && D != 64 && D != 80 && D != 96 && D != 128 && D != 256)
+        return fail(E, "fa_fwd: D must be 16, 32, 48, 64, 80, 96, 128 or 256, got %d", D);
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return fail(E, "fa_fwd: unknown dtype %d", (int)dtype);
     if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_ADDITIVE && mask_kind != FA_MASK_BOOL)
         return fail(E, "fa_fwd: unknown mask kind %d", (int)mask_kind);

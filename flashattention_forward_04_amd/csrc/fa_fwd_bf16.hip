@@ -161,9 +161,13 @@ fwd_bf16_kernel(const FwdParams p)
     constexpr int VTILE = VINS * 512;            // elements per V buffer
     constexpr int DK = D / 16;                   // k-steps of S^T over the head dimension
     constexpr int NC = BN / 32;                  // 32-key blocks per key tile
-    constexpr int ND = D / 32;                   // 32-wide blocks of O^T along the head dimension
+    // 32-wide blocks of O^T along the head dimension, rounded up: the rows
+    // past D of the last block read V^T columns past D (inside the padded
+    // LDS rows, never written) and are never stored
+    constexpr int ND = (D + 31) / 32;
     constexpr int NP = DK * NC;                  // score products per tile
-    static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+    static_assert(BN % 32 == 0 && D % 16 == 0, "tile shape");
+    static_assert(32 * ND <= D + 32, "the V^T reads of the last block stay inside a padded V row");
 
     // NB buffers each for K and V, as separate arrays so that the compiler
     // can tell the buffer being loaded from the ones being read
@@ -649,6 +653,7 @@ fwd_bf16_kernel(const FwdParams p)
         for (int d = 0; d < ND; ++d)
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
+                if (32 * d + 8 * rq >= D) continue;  // rows of the rounded-up last block
                 u32x2 w;
                 w[0] = pack_bf16x2(o[d][4 * rq + 0] * inv, o[d][4 * rq + 1] * inv);
                 w[1] = pack_bf16x2(o[d][4 * rq + 2] * inv, o[d][4 * rq + 3] * inv);
@@ -1233,6 +1238,24 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
 // Launch shapes per head dimension and mask use: waves per work-group, keys
 // per tile, waves per SIMD, pipelined (1) or not (0), LDS ring depth (2 or
 // 4).  Overridable at build time for tuning sweeps.
+#ifndef FA_BF16_D16_CFG
+#define FA_BF16_D16_CFG 4, 64, 2, 1, 2
+#endif
+#ifndef FA_BF16_D16_MASKED_CFG
+#define FA_BF16_D16_MASKED_CFG 4, 64, 2, 0, 2
+#endif
+#ifndef FA_BF16_D48_CFG
+#define FA_BF16_D48_CFG 4, 64, 2, 1, 2
+#endif
+#ifndef FA_BF16_D48_MASKED_CFG
+#define FA_BF16_D48_MASKED_CFG 4, 64, 2, 0, 2
+#endif
+#ifndef FA_BF16_D80_CFG
+#define FA_BF16_D80_CFG 8, 64, 2, 0, 2
+#endif
+#ifndef FA_BF16_D80_MASKED_CFG
+#define FA_BF16_D80_MASKED_CFG 8, 64, 2, 0, 2
+#endif
 #ifndef FA_BF16_D32_CFG
 #define FA_BF16_D32_CFG 4, 64, 2, 1, 2
 #endif
@@ -1282,8 +1305,11 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
 const Variant* variants_bf16(int* n)
 {
     static const Variant table[] = {
+    FA_BF16_FOR_D(16, FA_BF16_D16_CFG, FA_BF16_D16_MASKED_CFG),
     FA_BF16_FOR_D(32, FA_BF16_D32_CFG, FA_BF16_D32_MASKED_CFG),
+    FA_BF16_FOR_D(48, FA_BF16_D48_CFG, FA_BF16_D48_MASKED_CFG),
     FA_BF16_FOR_D(64, FA_BF16_D64_CFG, FA_BF16_D64_MASKED_CFG),
+    FA_BF16_FOR_D(80, FA_BF16_D80_CFG, FA_BF16_D80_MASKED_CFG),
     FA_BF16_FOR_D(96, FA_BF16_D96_CFG, FA_BF16_D96_MASKED_CFG),
     FA_BF16_FOR_D(128, FA_BF16_D128_CFG, FA_BF16_D128_MASKED_CFG),
     FA_BF16_FOR_D(256, FA_BF16_D256_CFG, FA_BF16_D256_MASKED_CFG),

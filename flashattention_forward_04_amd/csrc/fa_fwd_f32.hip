@@ -47,8 +47,12 @@ fwd_f32_kernel(const FwdParams p)
     constexpr int VP = BN + 4;  // V^T row pitch in LDS (floats)
     constexpr int DT = D / 8;   // groups of four k-steps over the head dimension
     constexpr int NC = BN / 32;
-    constexpr int ND = D / 32;
-    static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+    // 32-wide blocks of O^T; a head dim that is not a multiple of 32 is
+    // rounded up, and the extra rows of the last block (which only ever
+    // meet V^T rows past D) are never stored
+    constexpr int ND = (D + 31) / 32;
+    constexpr int DP = 32 * ND;  // V^T rows in LDS (the rows past D are read, never written)
+    static_assert(BN % 32 == 0 && D % 16 == 0, "tile shape");
 
     // two buffers each: K row-major (filled by direct global -> LDS loads,
     // padded to whole 1 KiB blocks) and V transposed (filled from registers)
@@ -56,8 +60,8 @@ fwd_f32_kernel(const FwdParams p)
     constexpr int KINS = (BN * KSPR + 63) / 64;  // 1 KiB blocks per K tile
     __shared__ __attribute__((aligned(1024))) float Ks0[KINS * 256];
     __shared__ __attribute__((aligned(1024))) float Ks1[KINS * 256];
-    __shared__ __attribute__((aligned(16))) float Vt0[D * VP];
-    __shared__ __attribute__((aligned(16))) float Vt1[D * VP];
+    __shared__ __attribute__((aligned(16))) float Vt0[DP * VP];
+    __shared__ __attribute__((aligned(16))) float Vt1[DP * VP];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -302,6 +306,7 @@ fwd_f32_kernel(const FwdParams p)
         for (int d = 0; d < ND; ++d)
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
+                if (32 * d + 8 * rq >= D) continue;  // rows of the rounded-up last block
                 const f32x4 w = f32x4{o[d][4 * rq + 0], o[d][4 * rq + 1], o[d][4 * rq + 2], o[d][4 * rq + 3]} * inv;
                 *(f32x4*)(orow + 32 * d + 8 * rq + 4 * g) = w;
             }
@@ -337,6 +342,15 @@ hipError_t launch_f32(const FwdParams& p, hipStream_t st)
 
 // Launch shapes per head dimension (waves per work-group, keys per tile);
 // overridable at build time for tuning sweeps.
+#ifndef FA_F32_D16_CFG
+#define FA_F32_D16_CFG 4, 32
+#endif
+#ifndef FA_F32_D48_CFG
+#define FA_F32_D48_CFG 4, 32
+#endif
+#ifndef FA_F32_D80_CFG
+#define FA_F32_D80_CFG 4, 64
+#endif
 #ifndef FA_F32_D32_CFG
 #define FA_F32_D32_CFG 4, 32
 #endif
@@ -360,8 +374,11 @@ hipError_t launch_f32(const FwdParams& p, hipStream_t st)
 const Variant* variants_f32(int* n)
 {
     static const Variant table[] = {
+    FA_F32_FOR_D_CFG(16, FA_F32_D16_CFG),
     FA_F32_FOR_D_CFG(32, FA_F32_D32_CFG),
+    FA_F32_FOR_D_CFG(48, FA_F32_D48_CFG),
     FA_F32_FOR_D_CFG(64, FA_F32_D64_CFG),
+    FA_F32_FOR_D_CFG(80, FA_F32_D80_CFG),
     FA_F32_FOR_D_CFG(96, FA_F32_D96_CFG),
     FA_F32_FOR_D_CFG(128, FA_F32_D128_CFG),
     FA_F32_FOR_D_CFG(256, FA_F32_D256_CFG),

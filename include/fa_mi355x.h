@@ -75,7 +75,7 @@ typedef enum {
  *
  * Checks (mlx-native flash_attn_train.rs, validate_params, plus this
  * library's own): B, H_q, H_kv, qL, kL > 0; H_q % H_kv == 0; D in
- * {32, 64, 96, 128, 256}; known dtype and mask kind; mask non-NULL iff a mask kind
+ * {16, 32, 48, 64, 80, 96, 128, 256}; known dtype and mask kind; mask non-NULL iff a mask kind
  * is given; Q, K, V, O, L non-NULL and 16-byte aligned; scale finite;
  * element counts fit in int64.
  */

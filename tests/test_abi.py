@@ -50,14 +50,14 @@ def test_version_and_status_strings(lib):
 
 def test_variant_table_covers_every_combination(lib):
     names = [fa.fa_variant_name(i) for i in range(fa.fa_variant_count())]
-    assert None not in names and len(set(names)) == len(names) == 60
+    assert None not in names and len(set(names)) == len(names) == 96
     assert fa.fa_variant_name(len(names)) is None and fa.fa_variant_name(-1) is None
     for dt in (fa.FA_DTYPE_F32, fa.FA_DTYPE_BF16):
-        for D in (32, 64, 96, 128, 256):
+        for D in (16, 32, 48, 64, 80, 96, 128, 256):
             for mk in (fa.FA_MASK_NONE, fa.FA_MASK_ADDITIVE, fa.FA_MASK_BOOL):
                 for c in (0, 1):
                     assert fa.fa_supported(dt, D, mk, c) == 1
-    assert fa.fa_supported(fa.FA_DTYPE_BF16, 80, fa.FA_MASK_NONE, 0) == 0
+    assert fa.fa_supported(fa.FA_DTYPE_BF16, 72, fa.FA_MASK_NONE, 0) == 0
     assert fa.fa_supported(7, 64, fa.FA_MASK_NONE, 0) == 0
 
 
@@ -71,8 +71,8 @@ BAD = [
     (dict(H_q=3), "divisible"),
     (dict(qL=0), "qL must be > 0"),
     (dict(kL=-1), "kL must be > 0"),
-    (dict(D=80), "D must be 32, 64, 96, 128 or 256"),
-    (dict(D=16), "D must be 32, 64, 96, 128 or 256"),
+    (dict(D=72), "D must be 16, 32, 48, 64, 80, 96, 128 or 256"),
+    (dict(D=8), "D must be 16, 32, 48, 64, 80, 96, 128 or 256"),
     (dict(dtype=5), "unknown dtype"),
     (dict(mask_kind=7, mask=P), "unknown mask kind"),
     (dict(mask_kind=fa.FA_MASK_ADDITIVE), "mask must be NULL exactly"),

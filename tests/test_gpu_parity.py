@@ -95,7 +95,7 @@ def _rand(shape, dtype, seed):
 
 
 @pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
-@pytest.mark.parametrize("D", [32, 64, 96, 128, 256])
+@pytest.mark.parametrize("D", [16, 32, 48, 64, 80, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 def test_head_dims_and_dtypes(dtype, D, causal):
     q = _rand((1, 4, 200, D), dtype, 1)
@@ -110,7 +110,7 @@ def test_head_dims_and_dtypes(dtype, D, causal):
 @pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("kind", ["additive", "bool"])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
-@pytest.mark.parametrize("D", [32, 64, 96])
+@pytest.mark.parametrize("D", [16, 32, 48, 64, 80, 96])
 def test_masks(dtype, kind, causal, D):
     q, k, v = _rand((2, 2, 70, D), dtype, 4), _rand((2, 2, 90, D), dtype, 5), _rand((2, 2, 90, D), dtype, 6)
     rng = np.random.default_rng(7)

@@ -77,12 +77,12 @@ SHORT_KL = [
     for kl in (32, 64, 128)
 ]
 
-# The headline shape at the two further head dims the kernels support
-# (D = 32 and 96): parity cases and benchmark workloads of their own.
+# The headline shape at the further head dims the kernels support: parity
+# cases and benchmark workloads of their own.
 HEAD_DIMS = [
     Workload(f"causal_bf16_d{d}_8k", "bf16", 1, 32, 8, 8192, 8192, d, 1 / math.sqrt(d), causal=True,
              seed=40 + d, note=f"long-context causal bf16 at head dim {d}")
-    for d in (32, 96)
+    for d in (16, 32, 48, 80, 96)
 ]
 
 # Ragged shapes that are not tile multiples (the configs above all are).
