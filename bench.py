@@ -185,7 +185,7 @@ def summarize(prof_dir, w, commands):
 
 
 def find_workload(W, name):
-    every = {x.name: x for x in (*W.CONFIGS.values(), *W.SHORT_KL, *W.HEAD_DIMS, *W.RAGGED)}
+    every = {x.name: x for x in (*W.CONFIGS.values(), *W.SHORT_KL, *W.HEAD_DIMS, *W.SPLIT_KV, *W.RAGGED)}
     if name not in every:
         raise SystemExit(f"unknown workload {name!r}; known: {', '.join(sorted(every))}")
     return every[name]

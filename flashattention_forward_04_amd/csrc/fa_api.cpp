@@ -130,6 +130,7 @@ fa_status fa_fwd_strided(const void* Q, const void* K, const void* V, const void
     const int vec_elems = 16 / esz;
     fa::FwdParams p;
     std::memset(&p, 0, sizeof(p));
+    p.n_split = 1;  // the kernels divide the grid by it: never 0
     fa_strides s;
     if (strides) s = *strides;
     else std::memset(&s, 0, sizeof(s));

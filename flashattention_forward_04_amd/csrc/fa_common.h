@@ -29,6 +29,15 @@ struct FwdParams {
     int neg_q;          // scale < 0: Q's sign bit is flipped on load instead
     int mask_vec;       // mask rows admit 4-element vector loads
     int pair_tiles;     // causal: the whole grid is resident at once (see causal_tile)
+    // Key range split over work-groups (n_split > 1): work-group s of a
+    // query tile takes key tiles [s * split_tiles, (s + 1) * split_tiles)
+    // and writes its normalised O (fp32, [n_split][B][H_q][qL][D]) and its
+    // natural-log L ([n_split][B][H_q][qL], -inf when no key of the range is
+    // allowed) to o_part / l_part; a merge kernel combines them.
+    float* o_part;
+    float* l_part;
+    int n_split;        // 1: no split
+    int split_tiles;
 };
 
 enum MaskKind { MASK_NONE = 0, MASK_ADD = 1, MASK_BOOL = 2 };

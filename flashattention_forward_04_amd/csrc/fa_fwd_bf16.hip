@@ -50,6 +50,7 @@
 
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 namespace fa {
@@ -105,6 +106,11 @@ constexpr float kRescaleSlack = 8.f;
 // tile (0 = leave it to the compiler).
 #ifndef FA_SCHED_S
 #define FA_SCHED_S 4
+#endif
+
+// Split long key ranges of small grids over work-groups (see launch_bf16).
+#ifndef FA_SPLIT_KV
+#define FA_SPLIT_KV 1
 #endif
 
 // K and V tiles live in LDS row-major ([BN][D], one key per row) with a
@@ -209,6 +215,8 @@ fwd_bf16_kernel(const FwdParams p)
     int id = blockIdx.x;
     const int h = head_of(id % p.Hq, p.Hq);
     id /= p.Hq;
+    const int split = id % p.n_split;
+    id /= p.n_split;
     const int b = id % p.B;
     id /= p.B;
     const int qt = CAUSAL ? causal_tile(id, p.n_qtiles, p.pair_tiles) : id;
@@ -237,10 +245,14 @@ fwd_bf16_kernel(const FwdParams p)
 
     const float c2 = p.scale_log2;
     const int kv_end = CAUSAL ? min(p.kL, min(p.qL, q0 + BM)) : p.kL;
-    const int n_tiles = (kv_end + BN - 1) / BN;
+    // key tiles of this query tile; a split work-group takes tiles
+    // [tb, tb + split_tiles) of them, numbered from 0 below
+    const int n_all = (kv_end + BN - 1) / BN;
+    const int tb = split * p.split_tiles;
+    const int n_tiles = max(0, (p.n_split > 1 ? min(n_all, tb + p.split_tiles) : n_all) - tb);
     // this wave needs tiles 0..t_last (a prefix: causal rows never see later keys)
     int t_last = n_tiles - 1;
-    if (CAUSAL) t_last = min(t_last, (wq0 + 31) / BN);
+    if (CAUSAL) t_last = min(t_last, (wq0 + 31) / BN - tb);
     if (wq0 >= p.qL) t_last = -1;
 
     // mask row of this lane (clamped so ragged rows read in bounds)
@@ -317,11 +329,11 @@ fwd_bf16_kernel(const FwdParams p)
             all_slots(std::false_type{});
     };
     auto issue_k = [&](int t, uint16_t* kt) __attribute__((always_inline)) {
-        issue_tile(Kb, p.k_s[2], t * BN, kt, koff, std::integral_constant<int, KSPR>{},
+        issue_tile(Kb, p.k_s[2], (tb + t) * BN, kt, koff, std::integral_constant<int, KSPR>{},
                    std::integral_constant<int, KINS>{});
     };
     auto issue_v = [&](int t, uint16_t* vt) __attribute__((always_inline)) {
-        issue_tile(Vb, p.v_s[2], t * BN, vt, voff, std::integral_constant<int, VSPR>{},
+        issue_tile(Vb, p.v_s[2], (tb + t) * BN, vt, voff, std::integral_constant<int, VSPR>{},
                    std::integral_constant<int, VINS>{});
     };
     // all of this wave's direct loads have landed in LDS
@@ -563,7 +575,7 @@ fwd_bf16_kernel(const FwdParams p)
     // softmax and P V of tile t with its scores in s
     auto finish_tile = [&](int t, f32x16 (&s)[NC], const uint16_t* vt, f32x16 (&sn)[NC], const uint16_t* kn,
                            const MaskWords& mw) __attribute__((always_inline)) {
-        const int j0 = t * BN;
+        const int j0 = (tb + t) * BN;
         const bool masked = (MASK != MASK_NONE) || (j0 + BN > p.kL) || (CAUSAL && j0 + BN - 1 > wq0);
         // one softmax for both kinds of tile, so that the accumulators and
         // the next tile's scores are written in one place (two copies of the
@@ -605,7 +617,7 @@ fwd_bf16_kernel(const FwdParams p)
         MaskWords& mn = (U & 1) ? ma : mb;
         if (t + PK < n_tiles) issue_k(t + PK, kbuf(std::integral_constant<int, (U + PK) % NB>{}));
         if (t + PV < n_tiles) issue_v(t + PV, vbuf(std::integral_constant<int, (U + PV) % NB>{}));
-        if (MASK != MASK_NONE && t + 1 <= t_last) load_mask((t + 1) * BN, mn);
+        if (MASK != MASK_NONE && t + 1 <= t_last) load_mask((tb + t + 1) * BN, mn);
         if (t <= t_last) {
             const uint16_t* vr = vbuf(std::integral_constant<int, U>{});
             if (PIPE) {
@@ -629,7 +641,7 @@ fwd_bf16_kernel(const FwdParams p)
         if (u < PK && u < n_tiles) issue_k(u, kbuf_dyn(u));
         if (u < PV && u < n_tiles) issue_v(u, vbuf_dyn(u));
     }
-    if (MASK != MASK_NONE && t_last >= 0) load_mask(0, ma);
+    if (MASK != MASK_NONE && t_last >= 0) load_mask(tb * BN, ma);
     wait_loads();
     __syncthreads();
     if (PIPE) {
@@ -646,7 +658,25 @@ fwd_bf16_kernel(const FwdParams p)
     }
 
     // ---- epilogue: O = O / l, L = (m + log2 l) ln2 (O = 0, L = 0 if no key) ----
-    if (qrow < p.qL) {
+    if (qrow < p.qL && p.n_split > 1) {
+        // one key range of a split launch: normalised fp32 O and natural-log
+        // L of this range (-inf when it holds no allowed key)
+        const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
+        const int64_t rows = (int64_t)p.B * p.Hq * p.qL;
+        const int64_t row = ((int64_t)b * p.Hq + h) * p.qL + qrow;
+        float* orow = p.o_part + ((int64_t)split * rows + row) * D;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                if (32 * d + 8 * rq >= D) continue;
+                *(f32x4*)(orow + 32 * d + 8 * rq + 4 * g) =
+                    f32x4{o[d][4 * rq + 0], o[d][4 * rq + 1], o[d][4 * rq + 2], o[d][4 * rq + 3]} * inv;
+            }
+        if (g == 0)
+            p.l_part[(int64_t)split * rows + row] =
+                (l_run > 0.f) ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : -INFINITY;
+    } else if (qrow < p.qL) {
         const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
         uint16_t* orow = (uint16_t*)p.o + b * p.o_s[0] + h * p.o_s[1] + (int64_t)qrow * p.o_s[2];
 #pragma unroll
@@ -666,6 +696,69 @@ fwd_bf16_kernel(const FwdParams p)
     }
 }
 
+// Merge of a split launch (one wave per query row): with L_s the natural-log
+// L of key range s, L = ln sum_s e^{L_s} and O = sum_s e^{L_s - L} O_s -- the
+// same combination the online softmax applies between key blocks, here on
+// normalised partials.  Ranges with no allowed key (L_s = -inf) weigh 0; a
+// row with none at all gets O = 0, L = 0.
+template <int D>
+__global__ void __launch_bounds__(256) merge_splits_bf16_kernel(const FwdParams p)
+{
+    constexpr int NE = (D + 63) / 64;  // head-dim elements per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t rows = (int64_t)p.B * p.Hq * p.qL;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int i = (int)(row % p.qL);
+    const int64_t bh = row / p.qL;
+    const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+    float lmax = -INFINITY;
+    for (int s = 0; s < p.n_split; ++s) lmax = fmaxf(lmax, p.l_part[s * rows + row]);
+    float sum = 0.f;
+    float acc[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[e] = 0.f;
+    if (lmax != -INFINITY) {
+        for (int s = 0; s < p.n_split; ++s) {
+            const float ls = p.l_part[s * rows + row];
+            if (ls == -INFINITY) continue;
+            const float w = __builtin_amdgcn_exp2f((ls - lmax) * kLog2e);
+            sum += w;
+            const float* src = p.o_part + (s * rows + row) * D;
+#pragma unroll
+            for (int e = 0; e < NE; ++e)
+                if (lane + 64 * e < D) acc[e] = __builtin_fmaf(w, src[lane + 64 * e], acc[e]);
+        }
+    }
+    const float inv = (sum > 0.f) ? 1.f / sum : 0.f;
+    uint16_t* orow = (uint16_t*)p.o + b * p.o_s[0] + h * p.o_s[1] + (int64_t)i * p.o_s[2];
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+        if (lane + 64 * e < D) orow[lane + 64 * e] = (uint16_t)(pack_bf16x2(acc[e] * inv, 0.f) & 0xffffu);
+    if (lane == 0) p.lse[row] = (sum > 0.f) ? lmax + __builtin_amdgcn_logf(sum) * kLn2 : 0.f;
+}
+
+// The device's default stream-ordered memory pool keeps up to this much
+// freed memory for reuse instead of returning it at every synchronisation
+// (split launches allocate their partials from it).
+constexpr uint64_t kPoolKeepBytes = 256ull << 20;
+
+inline hipError_t keep_pool_memory()
+{
+    static std::once_flag once[64];
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess || dev < 0 || dev >= 64) return err;
+    std::call_once(once[dev], [&]() {
+        hipMemPool_t pool;
+        if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+            uint64_t keep = kPoolKeepBytes;
+            hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        }
+    });
+    return hipSuccess;
+}
+
 template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB>
 hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
 {
@@ -673,12 +766,55 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
     // to 1 KiB blocks, NB buffers each for K and V)
     constexpr int kLdsPerWg = NB * ((BN * (D + 8) / 8 + 63) / 64 + (BN * (D + 32) / 8 + 63) / 64) * 1024;
     constexpr int kWgsPerCu = (4 * WPE / NW < 160 * 1024 / kLdsPerWg) ? 4 * WPE / NW : 160 * 1024 / kLdsPerWg;
+    constexpr int kCUs = 256;
     FwdParams q = p;
     const int64_t wgs = (int64_t)p.n_qtiles * p.Hq * p.B;
-    q.pair_tiles = CAUSAL && grid_fits_at_once(wgs, kWgsPerCu);
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB>), dim3((unsigned)wgs), dim3(NW * 64),
-                       0, st, q);
-    return hipGetLastError();
+    // A grid that leaves most CUs idle while each work-group walks a long key
+    // range splits that range over work-groups (at least kMinSplitTiles key
+    // tiles each, a multiple of the ring depth), up to one full GPU of
+    // work-groups, and merges the partials afterwards.
+    constexpr int kMinSplitTiles = 8;
+    const int kv_max = CAUSAL ? min(p.kL, p.qL) : p.kL;
+    const int n_kt = (kv_max + BN - 1) / BN;
+    int n_split = 1, split_tiles = 0;
+    if (FA_SPLIT_KV && wgs * 2 <= kCUs && n_kt >= 2 * kMinSplitTiles) {
+        const int64_t want = (int64_t)kCUs * kWgsPerCu / wgs;
+        const int by_len = n_kt / kMinSplitTiles;
+        const int s0 = (int)(want < by_len ? want : (int64_t)by_len);
+        if (s0 >= 2) {
+            split_tiles = (n_kt + s0 - 1) / s0;
+            split_tiles = (split_tiles + NB - 1) / NB * NB;
+            n_split = (n_kt + split_tiles - 1) / split_tiles;
+        }
+    }
+    if (n_split < 2) {
+        q.pair_tiles = CAUSAL && grid_fits_at_once(wgs, kWgsPerCu);
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB>), dim3((unsigned)wgs),
+                           dim3(NW * 64), 0, st, q);
+        return hipGetLastError();
+    }
+    // partials from the stream-ordered pool: freed (for reuse by later calls
+    // on this stream) once the merge has read them
+    const int64_t rows = (int64_t)p.B * p.Hq * p.qL;
+    void* ws = nullptr;
+    hipError_t err = keep_pool_memory();
+    if (err != hipSuccess) return err;
+    err = hipMallocAsync(&ws, (size_t)n_split * rows * (D + 1) * sizeof(float), st);
+    if (err != hipSuccess) return err;
+    q.o_part = (float*)ws;
+    q.l_part = q.o_part + (int64_t)n_split * rows * D;
+    q.n_split = n_split;
+    q.split_tiles = split_tiles;
+    q.pair_tiles = CAUSAL && grid_fits_at_once(wgs * n_split, kWgsPerCu);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB>), dim3((unsigned)(wgs * n_split)),
+                       dim3(NW * 64), 0, st, q);
+    err = hipGetLastError();
+    if (err == hipSuccess) {
+        hipLaunchKernelGGL((merge_splits_bf16_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, q);
+        err = hipGetLastError();
+    }
+    const hipError_t ferr = hipFreeAsync(ws, st);
+    return err != hipSuccess ? err : ferr;
 }
 
 // ---------------------------------------------------------------------------
@@ -1196,6 +1332,8 @@ constexpr int kShortKeys = 256;
 template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB>
 hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
 {
+    // the work-group kernel divides its grid index by n_split
+    if (p.n_split < 1) return hipErrorInvalidValue;
     if constexpr (D == 256) {
         constexpr int kCUs = 256;
         if ((int64_t)p.n_qtiles * p.Hq * p.B < kCUs) {

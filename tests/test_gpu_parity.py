@@ -74,7 +74,7 @@ def test_config_full_size_sampled(w, n_rows):
         assert np.array_equal(buf, np.transpose(O, (0, 2, 1, 3)).reshape(w.B, w.qL, w.Hq * w.D))
 
 
-@pytest.mark.parametrize("w", W.SHORT_KL, ids=lambda w: w.name)
+@pytest.mark.parametrize("w", W.SHORT_KL + W.SPLIT_KV, ids=lambda w: w.name)
 def test_short_key_shapes(w):
     """The HBM-bound short-key shapes at full size (the launch the benchmark
     times for them); oracle on sampled rows, every row finite."""
@@ -358,3 +358,39 @@ def test_tensors_past_2pow31_elements(kL, causal):
     print(f"[parity] large kL={kL}: max|dO| = {max(errs_o):.3e}, max|dL| = {max(errs_l):.3e} over {len(picks)} rows",
           flush=True)
     assert max(errs_o) <= TOL_O["bf16"] and max(errs_l) <= TOL_L
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,qL,kL,D,kind,causal", [
+    (1, 8, 2, 1, 4096, 128, "none", False),
+    (1, 8, 2, 16, 4100, 128, "none", False),
+    (2, 4, 4, 64, 3000, 64, "additive", False),
+    (1, 8, 8, 16, 4096, 128, "bool", False),
+    (1, 6, 3, 40, 5000, 96, "none", False),
+    (1, 4, 2, 24, 3333, 16, "additive", False),
+    (1, 2, 1, 2048, 2048, 128, "none", True),
+    (1, 2, 2, 1500, 1600, 64, "bool", True),
+], ids=lambda x: str(x))
+def test_key_range_split_over_work_groups(B, Hq, Hkv, qL, kL, D, kind, causal):
+    """Small grids with long key ranges: the key range is split over
+    work-groups and the partials merged (L = ln sum e^{L_s}).  Causal shapes
+    leave later ranges partly or wholly above the diagonal (empty ranges
+    weigh 0), and one row has no allowed key in any range."""
+    print(f"[case] split B={B} Hq={Hq} Hkv={Hkv} qL={qL} kL={kL} D={D} mask={kind} causal={causal}", flush=True)
+    q, k, v = _rand((B, Hq, qL, D), BF16, 41), _rand((B, Hkv, kL, D), BF16, 42), _rand((B, Hkv, kL, D), BF16, 43)
+    mask = None
+    if kind != "none":
+        rng = np.random.default_rng(44)
+        masked = W.draw_masked(rng, (B, Hq, qL, kL), 0.3)
+        masked[0, Hq - 1, qL // 2, :] = True  # no allowed key in any range
+        if kind == "bool":
+            mask = torch.from_numpy((~masked).astype(np.uint8))
+        else:
+            m = rng.standard_normal(masked.shape).astype(np.float32)
+            m[masked] = -np.inf
+            mask = torch.from_numpy(m).to(BF16)
+    scale = 1 / math.sqrt(D)
+    O, L, _ = run_gpu(q, k, v, mask, causal=causal, scale=scale)
+    Oref, Lref = run_oracle(q, k, v, mask, causal=causal, scale=scale)
+    assert_parity(O, L, Oref, Lref, "bf16", f"split qL={qL} kL={kL} D={D} {kind} causal={causal}")
+    if kind != "none":
+        assert np.all(O[0, Hq - 1, qL // 2] == 0) and L[0, Hq - 1, qL // 2] == 0

@@ -85,6 +85,14 @@ HEAD_DIMS = [
     for d in (16, 32, 48, 80, 96)
 ]
 
+# Short query ranges over long key ranges (a decode step): too few query
+# tiles to fill the GPU, so the key range is split over work-groups and the
+# partials merged.  HBM-bound: K and V dominate the bytes.
+SPLIT_KV = [
+    Workload("decode_bf16_d128_32k", "bf16", 1, 32, 8, 16, 32768, 128, 1 / math.sqrt(128), seed=60,
+             note="16 query rows over 32768 keys, bf16 D=128 (K/V-read bound)"),
+]
+
 # Ragged shapes that are not tile multiples (the configs above all are).
 RAGGED = [
     Workload("ragged_masked_d256", "bf16", 1, 2, 2, 1000, 3000, 256, 1 / 16, mask_kind="additive",
