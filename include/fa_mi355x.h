@@ -25,8 +25,13 @@
  *     owns all of them.  Q, K, V and the mask are read-only; O and L are
  *     overwritten in full (rows beyond qL and padding are never touched).
  *   - The call enqueues work on `hip_stream` (a hipStream_t; NULL = the null
- *     stream) and returns without synchronising.  The forward pass allocates
- *     no device memory.
+ *     stream) and returns without synchronising.  One case uses device
+ *     memory of its own: a bf16 call whose grid of query tiles leaves most
+ *     CUs idle while its key range is long splits that range over
+ *     work-groups.  It then takes fp32 partials (n_split * B * H_q * qL *
+ *     (D + 1) * 4 bytes) from the device's default stream-ordered memory
+ *     pool on `hip_stream` and returns them to the pool on the same stream
+ *     after the merge.  Every other call allocates nothing.
  *   - All argument checks run before any launch: a failed check writes
  *     nothing, launches nothing and returns FA_ERR_INVALID_ARGUMENT (or
  *     FA_ERR_UNSUPPORTED for a valid combination that is not built), with a
