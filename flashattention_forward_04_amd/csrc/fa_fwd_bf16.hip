@@ -759,34 +759,48 @@ inline hipError_t keep_pool_memory()
     return hipSuccess;
 }
 
+// Work-groups of the work-group kernel one CU holds: by waves per SIMD, and
+// by LDS (tiles padded to 1 KiB blocks, NB buffers each for K and V).
+template <int D, int NW, int BN, int WPE, int NB>
+constexpr int wgs_per_cu()
+{
+    constexpr int kLdsPerWg = NB * ((BN * (D + 8) / 8 + 63) / 64 + (BN * (D + 32) / 8 + 63) / 64) * 1024;
+    return (4 * WPE / NW < 160 * 1024 / kLdsPerWg) ? 4 * WPE / NW : 160 * 1024 / kLdsPerWg;
+}
+
+// How many work-groups a query tile's key range is split over (1: none).
+// A grid that leaves more than half of the CUs idle while each work-group
+// walks a long key range splits that range (at least kMinSplitTiles key
+// tiles each, a multiple of the ring depth), up to one full GPU of
+// work-groups; the partials are merged afterwards.
+template <bool CAUSAL, int BN, int NB>
+int split_plan(const FwdParams& p, int wgs_per_cu_, int* split_tiles)
+{
+    constexpr int kCUs = 256;
+    constexpr int kMinSplitTiles = 8;
+    const int64_t wgs = (int64_t)p.n_qtiles * p.Hq * p.B;
+    const int kv_max = CAUSAL ? min(p.kL, p.qL) : p.kL;
+    const int n_kt = (kv_max + BN - 1) / BN;
+    *split_tiles = 0;
+    if (!FA_SPLIT_KV || wgs * 2 > kCUs || n_kt < 2 * kMinSplitTiles) return 1;
+    const int64_t want = (int64_t)kCUs * wgs_per_cu_ / wgs;
+    const int by_len = n_kt / kMinSplitTiles;
+    const int s0 = (int)(want < by_len ? want : (int64_t)by_len);
+    if (s0 < 2) return 1;
+    int st = (n_kt + s0 - 1) / s0;
+    st = (st + NB - 1) / NB * NB;
+    *split_tiles = st;
+    return (n_kt + st - 1) / st;
+}
+
 template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB>
 hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
 {
-    // work-groups one CU holds: by waves per SIMD, and by LDS (tiles padded
-    // to 1 KiB blocks, NB buffers each for K and V)
-    constexpr int kLdsPerWg = NB * ((BN * (D + 8) / 8 + 63) / 64 + (BN * (D + 32) / 8 + 63) / 64) * 1024;
-    constexpr int kWgsPerCu = (4 * WPE / NW < 160 * 1024 / kLdsPerWg) ? 4 * WPE / NW : 160 * 1024 / kLdsPerWg;
-    constexpr int kCUs = 256;
+    constexpr int kWgsPerCu = wgs_per_cu<D, NW, BN, WPE, NB>();
     FwdParams q = p;
     const int64_t wgs = (int64_t)p.n_qtiles * p.Hq * p.B;
-    // A grid that leaves most CUs idle while each work-group walks a long key
-    // range splits that range over work-groups (at least kMinSplitTiles key
-    // tiles each, a multiple of the ring depth), up to one full GPU of
-    // work-groups, and merges the partials afterwards.
-    constexpr int kMinSplitTiles = 8;
-    const int kv_max = CAUSAL ? min(p.kL, p.qL) : p.kL;
-    const int n_kt = (kv_max + BN - 1) / BN;
-    int n_split = 1, split_tiles = 0;
-    if (FA_SPLIT_KV && wgs * 2 <= kCUs && n_kt >= 2 * kMinSplitTiles) {
-        const int64_t want = (int64_t)kCUs * kWgsPerCu / wgs;
-        const int by_len = n_kt / kMinSplitTiles;
-        const int s0 = (int)(want < by_len ? want : (int64_t)by_len);
-        if (s0 >= 2) {
-            split_tiles = (n_kt + s0 - 1) / s0;
-            split_tiles = (split_tiles + NB - 1) / NB * NB;
-            n_split = (n_kt + split_tiles - 1) / split_tiles;
-        }
-    }
+    int split_tiles = 0;
+    const int n_split = split_plan<CAUSAL, BN, NB>(p, kWgsPerCu, &split_tiles);
     if (n_split < 2) {
         q.pair_tiles = CAUSAL && grid_fits_at_once(wgs, kWgsPerCu);
         hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB>), dim3((unsigned)wgs),
@@ -1335,8 +1349,13 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
     // the work-group kernel divides its grid index by n_split
     if (p.n_split < 1) return hipErrorInvalidValue;
     if constexpr (D == 256) {
+        // Fewer query tiles than CUs: split the key range over work-groups
+        // when it is long enough (measured 73 against 80 us on 8 heads x
+        // 1024 rows x 3072 keys), else over the waves of one work-group.
         constexpr int kCUs = 256;
-        if ((int64_t)p.n_qtiles * p.Hq * p.B < kCUs) {
+        int split_tiles = 0;
+        if ((int64_t)p.n_qtiles * p.Hq * p.B < kCUs &&
+            split_plan<CAUSAL, BN, NB>(p, wgs_per_cu<D, NW, BN, WPE, NB>(), &split_tiles) < 2) {
             FwdParams q = p;
             q.n_qtiles = (p.qL + 31) / 32;
             q.pair_tiles = CAUSAL && grid_fits_at_once((int64_t)q.n_qtiles * q.Hq * q.B, 1);

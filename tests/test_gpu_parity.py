@@ -369,6 +369,8 @@ def test_tensors_past_2pow31_elements(kL, causal):
     (1, 4, 2, 24, 3333, 16, "additive", False),
     (1, 2, 1, 2048, 2048, 128, "none", True),
     (1, 2, 2, 1500, 1600, 64, "bool", True),
+    (1, 2, 2, 1024, 1100, 256, "bool", True),
+    (1, 3, 1, 200, 2000, 256, "additive", False),
 ], ids=lambda x: str(x))
 def test_key_range_split_over_work_groups(B, Hq, Hkv, qL, kL, D, kind, causal):
     """Small grids with long key ranges: the key range is split over
