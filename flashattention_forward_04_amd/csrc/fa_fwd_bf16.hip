@@ -1343,11 +1343,38 @@ fwd_bf16_stream_kernel(const FwdParams p, int wgs_per_head)
 // At D = 128, key ranges up to kShortKeys take a work-group shape suited to
 // HBM-bound launches.
 constexpr int kShortKeys = 256;
+// Query ranges up to this many rows take 2-wave work-groups.
+constexpr int kShortQueries = 64;
 template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB>
 hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
 {
     // the work-group kernel divides its grid index by n_split
     if (p.n_split < 1) return hipErrorInvalidValue;
+    if constexpr (D == 128) {
+        // Short key ranges are HBM-bound (Q in, O out).
+        if (MASK == MASK_NONE && p.kL <= 4 * 32) {
+            // streaming kernel: enough work-groups per kv head to fill the
+            // GPU twice over, each with at least a few query blocks per wave
+            constexpr int kResident = 2 * 256;
+            const int heads = p.B * p.Hkv;
+            const int blocks = p.group * ((p.qL + 31) / 32);
+            int per_head = (kResident + heads - 1) / heads;
+            per_head = max(1, min(per_head, blocks / 4));
+            const dim3 grid((unsigned)(per_head * heads));
+            hipLaunchKernelGGL((fwd_bf16_stream_kernel<D, CAUSAL, 4, 4>), grid, dim3(4 * 64), 0, st, p, per_head);
+            return hipGetLastError();
+        }
+    }
+    if constexpr (NW > 2) {
+        // Short query ranges (a decode step): 2-wave work-groups of 64 rows,
+        // so that waves are not spent on rows past qL and more work-groups
+        // fit per CU (the split plan then cuts a long key range finer).
+        if (p.qL <= kShortQueries) {
+            FwdParams q = p;
+            q.n_qtiles = (p.qL + 63) / 64;
+            return launch_bf16<D, MASK, CAUSAL, 2, BN, WPE, SCHED, NB>(q, st);
+        }
+    }
     if constexpr (D == 256) {
         // Fewer query tiles than CUs: split the key range over work-groups
         // when it is long enough (measured 73 against 80 us on 8 heads x
@@ -1365,22 +1392,10 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
         }
     }
     if constexpr (D == 128) {
-        // Short key ranges are HBM-bound (Q in, O out): 4-wave work-groups
-        // with 32-key tiles keep two work-groups per CU resident, so one's
-        // loads overlap the other's stores (kL = 32: 49 -> 38 us for
-        // 32 heads x 8192 rows); long ones keep the 8-wave shape.
-        if (MASK == MASK_NONE && p.kL <= 4 * 32) {
-            // streaming kernel: enough work-groups per kv head to fill the
-            // GPU twice over, each with at least a few query blocks per wave
-            constexpr int kResident = 2 * 256;
-            const int heads = p.B * p.Hkv;
-            const int blocks = p.group * ((p.qL + 31) / 32);
-            int per_head = (kResident + heads - 1) / heads;
-            per_head = max(1, min(per_head, blocks / 4));
-            const dim3 grid((unsigned)(per_head * heads));
-            hipLaunchKernelGGL((fwd_bf16_stream_kernel<D, CAUSAL, 4, 4>), grid, dim3(4 * 64), 0, st, p, per_head);
-            return hipGetLastError();
-        }
+        // Key ranges up to kShortKeys: 4-wave work-groups with 32-key tiles
+        // keep two work-groups per CU resident, so one's loads overlap the
+        // other's stores (kL = 32: 49 -> 38 us for 32 heads x 8192 rows);
+        // long ones keep the 8-wave shape.
         if (p.kL <= kShortKeys) {
             FwdParams q = p;
             q.n_qtiles = (p.qL + 127) / 128;
