@@ -38,6 +38,9 @@ struct FwdParams {
     float* l_part;
     int n_split;        // 1: no split
     int split_tiles;
+    // Work-group kernel: rows [32 t, 32 t + 32) of NW query heads of one GQA
+    // group per work-group, one head per wave (short query ranges).
+    int head_pack;
 };
 
 enum MaskKind { MASK_NONE = 0, MASK_ADD = 1, MASK_BOOL = 2 };

@@ -212,18 +212,41 @@ fwd_bf16_kernel(const FwdParams p)
     const int g = lane >> 5;
 
     // ---- which (query tile, head, batch) this work-group owns ----
+    // Normally one query head and NW * 32 consecutive rows.  With head_pack
+    // (a query range of at most 32 rows in a GQA group) rows [q0, q0 + 32) of
+    // NW query heads of one kv head's group: wave w takes the w-th of them,
+    // so the heads share every K/V tile the work-group stages.
     int id = blockIdx.x;
-    const int h = head_of(id % p.Hq, p.Hq);
-    id /= p.Hq;
-    const int split = id % p.n_split;
-    id /= p.n_split;
-    const int b = id % p.B;
-    id /= p.B;
-    const int qt = CAUSAL ? causal_tile(id, p.n_qtiles, p.pair_tiles) : id;
-    const int q0 = qt * BM;
-    const int hk = h / p.group;
-    const int wq0 = q0 + wave * 32;  // first query row of this wave
-    const int qrow = wq0 + r32;      // this lane's query row
+    int h, hk, split, b, q0, wq0;
+    bool head_ok = true;  // false: a packed wave past the end of its group
+    if (p.head_pack) {
+        const int nch = (p.group + NW - 1) / NW;
+        const int c = id % nch;
+        id /= nch;
+        hk = id % p.Hkv;
+        id /= p.Hkv;
+        split = id % p.n_split;
+        id /= p.n_split;
+        b = id % p.B;
+        id /= p.B;
+        q0 = id * 32;
+        const int hg = c * NW + wave;
+        head_ok = hg < p.group;
+        h = hk * p.group + min(hg, p.group - 1);
+        wq0 = q0;
+    } else {
+        h = head_of(id % p.Hq, p.Hq);
+        id /= p.Hq;
+        split = id % p.n_split;
+        id /= p.n_split;
+        b = id % p.B;
+        id /= p.B;
+        const int qt = CAUSAL ? causal_tile(id, p.n_qtiles, p.pair_tiles) : id;
+        q0 = qt * BM;
+        hk = h / p.group;
+        wq0 = q0 + wave * 32;  // first query row of this wave
+    }
+    const int qrow = wq0 + r32;  // this lane's query row
 
     const uint16_t* Qb = (const uint16_t*)p.q + b * p.q_s[0] + h * p.q_s[1];
     const uint16_t* Kb = (const uint16_t*)p.k + b * p.k_s[0] + hk * p.k_s[1];
@@ -232,7 +255,7 @@ fwd_bf16_kernel(const FwdParams p)
     // ---- Q fragments: row qrow, elements 16ks + 8g .. +7 (zeros past qL) ----
     bf16x8 qf[DK];
     {
-        const bool in = qrow < p.qL;
+        const bool in = head_ok && qrow < p.qL;
         const u32x4* src = (const u32x4*)(Qb + (int64_t)(in ? qrow : 0) * p.q_s[2]);
         const uint32_t flip = p.neg_q ? 0x80008000u : 0u;
 #pragma unroll
@@ -244,7 +267,7 @@ fwd_bf16_kernel(const FwdParams p)
     }
 
     const float c2 = p.scale_log2;
-    const int kv_end = CAUSAL ? min(p.kL, min(p.qL, q0 + BM)) : p.kL;
+    const int kv_end = CAUSAL ? min(p.kL, min(p.qL, q0 + (p.head_pack ? 32 : BM))) : p.kL;
     // key tiles of this query tile; a split work-group takes tiles
     // [tb, tb + split_tiles) of them, numbered from 0 below
     const int n_all = (kv_end + BN - 1) / BN;
@@ -253,7 +276,7 @@ fwd_bf16_kernel(const FwdParams p)
     // this wave needs tiles 0..t_last (a prefix: causal rows never see later keys)
     int t_last = n_tiles - 1;
     if (CAUSAL) t_last = min(t_last, (wq0 + 31) / BN - tb);
-    if (wq0 >= p.qL) t_last = -1;
+    if (wq0 >= p.qL || !head_ok) t_last = -1;
 
     // mask row of this lane (clamped so ragged rows read in bounds)
     const uint8_t* mrow = nullptr;
@@ -658,7 +681,7 @@ fwd_bf16_kernel(const FwdParams p)
     }
 
     // ---- epilogue: O = O / l, L = (m + log2 l) ln2 (O = 0, L = 0 if no key) ----
-    if (qrow < p.qL && p.n_split > 1) {
+    if (qrow < p.qL && head_ok && p.n_split > 1) {
         // one key range of a split launch: normalised fp32 O and natural-log
         // L of this range (-inf when it holds no allowed key)
         const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
@@ -676,7 +699,7 @@ fwd_bf16_kernel(const FwdParams p)
         if (g == 0)
             p.l_part[(int64_t)split * rows + row] =
                 (l_run > 0.f) ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : -INFINITY;
-    } else if (qrow < p.qL) {
+    } else if (qrow < p.qL && head_ok) {
         const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
         uint16_t* orow = (uint16_t*)p.o + b * p.o_s[0] + h * p.o_s[1] + (int64_t)qrow * p.o_s[2];
 #pragma unroll
@@ -774,11 +797,10 @@ constexpr int wgs_per_cu()
 // tiles each, a multiple of the ring depth), up to one full GPU of
 // work-groups; the partials are merged afterwards.
 template <bool CAUSAL, int BN, int NB>
-int split_plan(const FwdParams& p, int wgs_per_cu_, int* split_tiles)
+int split_plan(const FwdParams& p, int64_t wgs, int wgs_per_cu_, int* split_tiles)
 {
     constexpr int kCUs = 256;
     constexpr int kMinSplitTiles = 8;
-    const int64_t wgs = (int64_t)p.n_qtiles * p.Hq * p.B;
     const int kv_max = CAUSAL ? min(p.kL, p.qL) : p.kL;
     const int n_kt = (kv_max + BN - 1) / BN;
     *split_tiles = 0;
@@ -798,9 +820,10 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
 {
     constexpr int kWgsPerCu = wgs_per_cu<D, NW, BN, WPE, NB>();
     FwdParams q = p;
-    const int64_t wgs = (int64_t)p.n_qtiles * p.Hq * p.B;
+    const int64_t wgs = p.head_pack ? (int64_t)p.n_qtiles * ((p.group + NW - 1) / NW) * p.Hkv * p.B
+                                    : (int64_t)p.n_qtiles * p.Hq * p.B;
     int split_tiles = 0;
-    const int n_split = split_plan<CAUSAL, BN, NB>(p, kWgsPerCu, &split_tiles);
+    const int n_split = split_plan<CAUSAL, BN, NB>(p, wgs, kWgsPerCu, &split_tiles);
     if (n_split < 2) {
         q.pair_tiles = CAUSAL && grid_fits_at_once(wgs, kWgsPerCu);
         hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB>), dim3((unsigned)wgs),
@@ -1371,7 +1394,13 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
         // fit per CU (the split plan then cuts a long key range finer).
         if (p.qL <= kShortQueries) {
             FwdParams q = p;
-            q.n_qtiles = (p.qL + 63) / 64;
+            if (p.qL <= 32 && p.group >= 2) {
+                // one 32-row tile: pack two query heads of a GQA group
+                q.head_pack = 1;
+                q.n_qtiles = 1;
+            } else {
+                q.n_qtiles = (p.qL + 63) / 64;
+            }
             return launch_bf16<D, MASK, CAUSAL, 2, BN, WPE, SCHED, NB>(q, st);
         }
     }
@@ -1382,7 +1411,8 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
         constexpr int kCUs = 256;
         int split_tiles = 0;
         if ((int64_t)p.n_qtiles * p.Hq * p.B < kCUs &&
-            split_plan<CAUSAL, BN, NB>(p, wgs_per_cu<D, NW, BN, WPE, NB>(), &split_tiles) < 2) {
+            split_plan<CAUSAL, BN, NB>(p, (int64_t)p.n_qtiles * p.Hq * p.B, wgs_per_cu<D, NW, BN, WPE, NB>(),
+                                       &split_tiles) < 2) {
             FwdParams q = p;
             q.n_qtiles = (p.qL + 31) / 32;
             q.pair_tiles = CAUSAL && grid_fits_at_once((int64_t)q.n_qtiles * q.Hq * q.B, 1);

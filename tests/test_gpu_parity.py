@@ -396,3 +396,38 @@ def test_key_range_split_over_work_groups(B, Hq, Hkv, qL, kL, D, kind, causal):
     assert_parity(O, L, Oref, Lref, "bf16", f"split qL={qL} kL={kL} D={D} {kind} causal={causal}")
     if kind != "none":
         assert np.all(O[0, Hq - 1, qL // 2] == 0) and L[0, Hq - 1, qL // 2] == 0
+
+
+@pytest.mark.parametrize("Hq,Hkv,qL,kL,D,kind,causal", [
+    (8, 4, 1, 4096, 128, "none", False),
+    (8, 2, 17, 3000, 128, "additive", False),
+    (9, 3, 32, 5000, 64, "none", False),
+    (32, 4, 5, 2500, 96, "bool", False),
+    (4, 2, 32, 100, 128, "none", False),
+    (6, 2, 20, 333, 256, "additive", False),
+    (4, 1, 32, 32, 64, "none", True),
+    (8, 2, 24, 1000, 128, "bool", True),
+], ids=lambda x: str(x))
+def test_short_query_ranges_pack_gqa_heads(Hq, Hkv, qL, kL, D, kind, causal):
+    """At most 32 query rows in a GQA group: one work-group takes the rows of
+    two query heads of the group (one per wave; a group of odd size leaves a
+    wave idle), with and without a split of the key range."""
+    print(f"[case] pack Hq={Hq} Hkv={Hkv} qL={qL} kL={kL} D={D} mask={kind} causal={causal}", flush=True)
+    q, k, v = _rand((2, Hq, qL, D), BF16, 51), _rand((2, Hkv, kL, D), BF16, 52), _rand((2, Hkv, kL, D), BF16, 53)
+    mask = None
+    if kind != "none":
+        rng = np.random.default_rng(54)
+        masked = W.draw_masked(rng, (2, Hq, qL, kL), 0.3)
+        masked[1, Hq - 1, qL - 1, :] = True  # no allowed key
+        if kind == "bool":
+            mask = torch.from_numpy((~masked).astype(np.uint8))
+        else:
+            m = rng.standard_normal(masked.shape).astype(np.float32)
+            m[masked] = -np.inf
+            mask = torch.from_numpy(m).to(BF16)
+    scale = 1 / math.sqrt(D)
+    O, L, _ = run_gpu(q, k, v, mask, causal=causal, scale=scale)
+    Oref, Lref = run_oracle(q, k, v, mask, causal=causal, scale=scale)
+    assert_parity(O, L, Oref, Lref, "bf16", f"pack Hq={Hq}/{Hkv} qL={qL} kL={kL} D={D} {kind} causal={causal}")
+    if kind != "none":
+        assert np.all(O[1, Hq - 1, qL - 1] == 0) and L[1, Hq - 1, qL - 1] == 0
