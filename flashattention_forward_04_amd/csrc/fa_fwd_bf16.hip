@@ -735,18 +735,27 @@ __global__ void __launch_bounds__(256) merge_splits_bf16_kernel(const FwdParams 
     const int i = (int)(row % p.qL);
     const int64_t bh = row / p.qL;
     const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+    // the largest L_s and sum_s e^{L_s - max}: the splits spread over the
+    // lanes, then reduced across the wave
     float lmax = -INFINITY;
-    for (int s = 0; s < p.n_split; ++s) lmax = fmaxf(lmax, p.l_part[s * rows + row]);
-    float sum = 0.f;
+    for (int s = lane; s < p.n_split; s += 64) lmax = fmaxf(lmax, p.l_part[s * rows + row]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, m));
     float acc[NE];
 #pragma unroll
     for (int e = 0; e < NE; ++e) acc[e] = 0.f;
+    float sum = 0.f;
     if (lmax != -INFINITY) {
+        for (int s = lane; s < p.n_split; s += 64)
+            sum += __builtin_amdgcn_exp2f((p.l_part[s * rows + row] - lmax) * kLog2e);
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
+        // O = sum_s e^{L_s - max} O_s / sum; an empty range has L_s = -inf
+        // and weighs exactly 0.  Unrolled so that the partial rows of several
+        // splits are in flight together.
+#pragma unroll 8
         for (int s = 0; s < p.n_split; ++s) {
-            const float ls = p.l_part[s * rows + row];
-            if (ls == -INFINITY) continue;
-            const float w = __builtin_amdgcn_exp2f((ls - lmax) * kLog2e);
-            sum += w;
+            const float w = __builtin_amdgcn_exp2f((p.l_part[s * rows + row] - lmax) * kLog2e);
             const float* src = p.o_part + (s * rows + row) * D;
 #pragma unroll
             for (int e = 0; e < NE; ++e)
