@@ -220,11 +220,13 @@ fwd_bf16_kernel(const FwdParams p)
     int h, hk, split, b, q0, wq0;
     bool head_ok = true;  // false: a packed wave past the end of its group
     if (p.head_pack) {
+        // kv head innermost: the work-groups of one kv head's group sit H_kv
+        // ids apart, on one XCD (one L2) when H_kv is a multiple of 8
         const int nch = (p.group + NW - 1) / NW;
-        const int c = id % nch;
-        id /= nch;
         hk = id % p.Hkv;
         id /= p.Hkv;
+        const int c = id % nch;
+        id /= nch;
         split = id % p.n_split;
         id /= p.n_split;
         b = id % p.B;
