@@ -46,6 +46,22 @@
  * attends).
  *
  * Returns 0, or -1 when an argument is out of range.
+ *
+ * Dropout (fa_oracle_fwd_dropout; ruDNN dense_attention.rs, `keep`,
+ * `keep_global` and the `dropout` branch of `forward_flash`): each allowed
+ * term of the P V sum is multiplied by k_ij / (1 - p), where k_ij = 1 when a
+ * uniform u_ij >= p and 0 otherwise (all 0 when p >= 1).  The denominator
+ * l_i and hence L are those without dropout.  u_ij comes from the position
+ * n = ((b*Hq + h)*qL + i)*kL + j: the Philox-4x32 block cipher with 10
+ * rounds (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy
+ * as 1, 2, 3", SC 2011) is applied to the 128-bit counter
+ * (offset + floor(n / 4), 64-bit, low word first; then two zero words)
+ * under the 64-bit key `seed` (low word first); word n mod 4 of the result,
+ * w, gives u = floor(w / 2^8) / 2^24.
+ * The generator's output stream is pinned by its properties only (a
+ * bijection per key, uniform words, the keep rate); no independent
+ * implementation of Philox-4x32 is available here: parity unpinned for the
+ * exact stream.
  */
 #include <math.h>
 #include <stdint.h>
@@ -63,11 +79,55 @@ int fa_oracle_threads(void)
 #endif
 }
 
+/* One Philox-4x32 round function, then the key schedule, 10 times: the
+ * two 32x32 -> 64-bit products of words 0 and 2 with the round multipliers
+ * are spread over the four words as (hi(c2 M1) ^ c1 ^ k0, lo(c2 M1),
+ * hi(c0 M0) ^ c3 ^ k1, lo(c0 M0)); the key words advance by the Weyl
+ * increments (the golden ratio and sqrt(3) - 1, as 32-bit fractions). */
+void fa_oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    const uint64_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+    const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        const uint64_t p0 = M0 * (uint64_t)c0;
+        const uint64_t p1 = M1 * (uint64_t)c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n1 = (uint32_t)p1;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n3 = (uint32_t)p0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+        k0 += W0;
+        k1 += W1;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* k_n / (1 - p) for score position n (see the header): 0 or 1 / (1 - p). */
+double fa_oracle_dropout_multiplier(int64_t n, float p, uint64_t seed, uint64_t offset)
+{
+    if (!(p < 1.0f)) return 0.0;
+    const uint64_t ctr64 = offset + (uint64_t)(n / 4);
+    const uint32_t ctr[4] = {(uint32_t)ctr64, (uint32_t)(ctr64 >> 32), 0u, 0u};
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t w[4];
+    fa_oracle_philox4x32_10(ctr, key, w);
+    const double u = (double)(w[n % 4] >> 8) / 16777216.0;
+    return (u >= (double)p) ? 1.0 / (1.0 - (double)p) : 0.0;
+}
+
+typedef struct {
+    int on;
+    float p;
+    uint64_t seed, offset;
+} dropout_t;
+
 static void one_row(const double* Q, const double* K, const double* V,
                     const double* mask, int mask_kind,
                     int Hq, int Hkv, int qL, int kL, int D, double scale,
                     int causal, int64_t flat, double* s, unsigned char* ok,
-                    double* o, double* lse)
+                    double* o, double* lse, const dropout_t* drop)
 {
     const int64_t i = flat % qL;
     const int64_t bh = flat / qL;
@@ -116,19 +176,22 @@ static void one_row(const double* Q, const double* K, const double* V,
         if (!ok[j]) continue;
         const double p = exp(s[j] - m);
         l += p;
+        const double pv = drop->on ? p * fa_oracle_dropout_multiplier(flat * kL + j, drop->p, drop->seed,
+                                                                      drop->offset)
+                                   : p;
         const double* v = vbase + j * D;
-        for (int d = 0; d < D; ++d) o[d] += p * v[d];
+        for (int d = 0; d < D; ++d) o[d] += pv * v[d];
     }
     for (int d = 0; d < D; ++d) o[d] = o[d] / l;
     *lse = m + log(l);
 }
 
-int fa_oracle_fwd(const double* Q, const double* K, const double* V,
-                  const double* mask, int mask_kind,
-                  int B, int Hq, int Hkv, int qL, int kL, int D,
-                  double scale, int causal,
-                  const int64_t* rows, int64_t nrows,
-                  double* O, double* L)
+static int run_rows(const double* Q, const double* K, const double* V,
+                    const double* mask, int mask_kind,
+                    int B, int Hq, int Hkv, int qL, int kL, int D,
+                    double scale, int causal,
+                    const int64_t* rows, int64_t nrows,
+                    double* O, double* L, const dropout_t* drop)
 {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || qL <= 0 || kL <= 0 || D <= 0) return -1;
     if (Hq % Hkv != 0) return -1;
@@ -152,11 +215,37 @@ int fa_oracle_fwd(const double* Q, const double* K, const double* V,
             for (int64_t r = 0; r < nrows; ++r) {
                 const int64_t flat = rows ? rows[r] : r;
                 one_row(Q, K, V, mask, mask_kind, Hq, Hkv, qL, kL, D, scale,
-                        causal, flat, s, ok, O + r * D, L + r);
+                        causal, flat, s, ok, O + r * D, L + r, drop);
             }
         }
         free(s);
         free(ok);
     }
     return bad ? -1 : 0;
+}
+
+int fa_oracle_fwd(const double* Q, const double* K, const double* V,
+                  const double* mask, int mask_kind,
+                  int B, int Hq, int Hkv, int qL, int kL, int D,
+                  double scale, int causal,
+                  const int64_t* rows, int64_t nrows,
+                  double* O, double* L)
+{
+    const dropout_t none = {0, 0.0f, 0, 0};
+    return run_rows(Q, K, V, mask, mask_kind, B, Hq, Hkv, qL, kL, D, scale, causal, rows, nrows, O, L, &none);
+}
+
+/* fa_oracle_fwd with dropout of rate p (0 <= p <= 1) under `seed` and
+ * counter `offset` (see the header). */
+int fa_oracle_fwd_dropout(const double* Q, const double* K, const double* V,
+                          const double* mask, int mask_kind,
+                          int B, int Hq, int Hkv, int qL, int kL, int D,
+                          double scale, int causal,
+                          const int64_t* rows, int64_t nrows,
+                          double* O, double* L,
+                          float p, uint64_t seed, uint64_t offset)
+{
+    if (!(p >= 0.0f && p <= 1.0f)) return -1;
+    const dropout_t drop = {1, p, seed, offset};
+    return run_rows(Q, K, V, mask, mask_kind, B, Hq, Hkv, qL, kL, D, scale, causal, rows, nrows, O, L, &drop);
 }

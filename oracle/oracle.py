@@ -44,12 +44,34 @@ class OracleLib:
                       ctypes.c_int, ctypes.c_double, ctypes.c_int,
                       ctypes.POINTER(ctypes.c_int64), ctypes.c_int64, dp, dp]
         f.restype = ctypes.c_int
+        fd = self.lib.fa_oracle_fwd_dropout
+        fd.argtypes = list(f.argtypes) + [ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64]
+        fd.restype = ctypes.c_int
+        u32p = ctypes.POINTER(ctypes.c_uint32)
+        self.lib.fa_oracle_philox4x32_10.argtypes = [u32p, u32p, u32p]
+        self.lib.fa_oracle_philox4x32_10.restype = None
+        self.lib.fa_oracle_dropout_multiplier.argtypes = [ctypes.c_int64, ctypes.c_float, ctypes.c_uint64,
+                                                          ctypes.c_uint64]
+        self.lib.fa_oracle_dropout_multiplier.restype = ctypes.c_double
         self.lib.fa_oracle_threads.restype = ctypes.c_int
 
     def threads(self) -> int:
         return int(self.lib.fa_oracle_threads())
 
-    def fwd(self, q, k, v, *, scale, causal=False, mask=None, mask_kind="none", rows=None):
+    def philox4x32_10(self, ctr, key):
+        """The Philox-4x32-10 block (4 words) for a 4-word counter and a 2-word key."""
+        c = (ctypes.c_uint32 * 4)(*[int(x) & 0xFFFFFFFF for x in ctr])
+        k = (ctypes.c_uint32 * 2)(*[int(x) & 0xFFFFFFFF for x in key])
+        o = (ctypes.c_uint32 * 4)()
+        self.lib.fa_oracle_philox4x32_10(c, k, o)
+        return [int(x) for x in o]
+
+    def dropout_multiplier(self, n, p, seed, offset=0):
+        """k_n / (1 - p) for score position n (0 when dropped)."""
+        return float(self.lib.fa_oracle_dropout_multiplier(int(n), float(p), int(seed), int(offset)))
+
+    def fwd(self, q, k, v, *, scale, causal=False, mask=None, mask_kind="none", rows=None,
+            dropout_p=None, seed=0, offset=0):
         """Attention forward in fp64.
 
         q [B,Hq,qL,D], k/v [B,Hkv,kL,D]; mask broadcastable to [B,Hq,qL,kL]
@@ -86,9 +108,13 @@ class OracleLib:
         O = np.empty((n, D), dtype=np.float64)
         L = np.empty((n,), dtype=np.float64)
         dp = ctypes.POINTER(ctypes.c_double)
-        rc = self.lib.fa_oracle_fwd(q.ctypes.data_as(dp), k.ctypes.data_as(dp), v.ctypes.data_as(dp),
-                                    mptr, kind, B, Hq, Hkv, qL, kL, D, float(scale), int(bool(causal)),
-                                    rptr, n, O.ctypes.data_as(dp), L.ctypes.data_as(dp))
+        args = (q.ctypes.data_as(dp), k.ctypes.data_as(dp), v.ctypes.data_as(dp),
+                mptr, kind, B, Hq, Hkv, qL, kL, D, float(scale), int(bool(causal)),
+                rptr, n, O.ctypes.data_as(dp), L.ctypes.data_as(dp))
+        if dropout_p is None:
+            rc = self.lib.fa_oracle_fwd(*args)
+        else:
+            rc = self.lib.fa_oracle_fwd_dropout(*args, float(dropout_p), int(seed), int(offset))
         if rc != 0:
             raise ValueError("oracle: fa_oracle_fwd rejected its arguments")
         if rows is None:
@@ -106,9 +132,20 @@ def _default() -> OracleLib:
     return _DEFAULT
 
 
-def attention_fwd(q, k, v, *, scale, causal=False, mask=None, mask_kind="none", rows=None):
-    """fp64 attention forward with the default compiled oracle (see OracleLib.fwd)."""
-    return _default().fwd(q, k, v, scale=scale, causal=causal, mask=mask, mask_kind=mask_kind, rows=rows)
+def attention_fwd(q, k, v, *, scale, causal=False, mask=None, mask_kind="none", rows=None,
+                  dropout_p=None, seed=0, offset=0):
+    """fp64 attention forward with the default compiled oracle (see OracleLib.fwd).  With
+    dropout_p set, each P V term is scaled by its keep decision / (1 - p) (L is unchanged)."""
+    return _default().fwd(q, k, v, scale=scale, causal=causal, mask=mask, mask_kind=mask_kind, rows=rows,
+                          dropout_p=dropout_p, seed=seed, offset=offset)
+
+
+def philox4x32_10(ctr, key):
+    return _default().philox4x32_10(ctr, key)
+
+
+def dropout_multiplier(n, p, seed, offset=0):
+    return _default().dropout_multiplier(n, p, seed, offset)
 
 
 def oracle_threads() -> int:
