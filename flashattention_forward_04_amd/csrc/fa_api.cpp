@@ -30,10 +30,17 @@ fa_status fail(fa_status st, const char* fmt, ...)
     return st;
 }
 
-const fa::Variant* find_variant(int dtype, int D, int mask, int causal)
+// Dropout of a fa_fwd_dropout call.
+struct DropArgs {
+    float p;
+    uint64_t seed, offset;
+};
+
+const fa::Variant* find_variant(int dtype, int D, int mask, int causal, bool dropout = false)
 {
     int n = 0;
-    const fa::Variant* tab = dtype == FA_DTYPE_BF16 ? fa::variants_bf16(&n) : fa::variants_f32(&n);
+    const fa::Variant* tab = dropout ? (dtype == FA_DTYPE_BF16 ? fa::variants_bf16_dropout(&n) : nullptr)
+                             : dtype == FA_DTYPE_BF16 ? fa::variants_bf16(&n) : fa::variants_f32(&n);
     for (int i = 0; i < n; ++i)
         if (tab[i].D == D && tab[i].mask == mask && tab[i].causal == (causal ? 1 : 0)) return &tab[i];
     return nullptr;
@@ -97,12 +104,16 @@ int fa_supported(fa_dtype dtype, int D, fa_mask_kind mask_kind, int causal)
     return find_variant(dtype, D, mask_kind, causal) != nullptr;
 }
 
-fa_status fa_fwd_strided(const void* Q, const void* K, const void* V, const void* mask,
-                         void* O, float* L,
-                         int B, int H_q, int H_kv, int qL, int kL, int D,
-                         float scale, int causal,
-                         fa_dtype dtype, fa_mask_kind mask_kind,
-                         const fa_strides* strides, void* hip_stream)
+}  // extern "C"
+
+namespace {
+
+fa_status fwd_impl(const void* Q, const void* K, const void* V, const void* mask,
+                   void* O, float* L,
+                   int B, int H_q, int H_kv, int qL, int kL, int D,
+                   float scale, int causal,
+                   fa_dtype dtype, fa_mask_kind mask_kind,
+                   const fa_strides* strides, void* hip_stream, const DropArgs* drop)
 {
     g_last_error[0] = '\0';
     const fa_status E = FA_ERR_INVALID_ARGUMENT;
@@ -121,6 +132,8 @@ fa_status fa_fwd_strided(const void* Q, const void* K, const void* V, const void
         return fail(E, "fa_fwd: mask must be NULL exactly when mask_kind is FA_MASK_NONE");
     if (!Q || !K || !V || !O || !L) return fail(E, "fa_fwd: Q, K, V, O and L must be non-NULL");
     if (!std::isfinite(scale)) return fail(E, "fa_fwd: scale must be finite");
+    if (drop && !(drop->p >= 0.f && drop->p <= 1.f))
+        return fail(E, "fa_fwd_dropout: the dropout rate must lie in [0, 1], got %g", (double)drop->p);
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(L, 4))
         return fail(E, "fa_fwd: Q, K, V and O must be 16-byte aligned and L 4-byte aligned");
     if ((int64_t)B * H_q * qL * D > INT64_MAX / 8 || (int64_t)B * H_q * qL * kL > INT64_MAX / 8)
@@ -131,6 +144,14 @@ fa_status fa_fwd_strided(const void* Q, const void* K, const void* V, const void
     fa::FwdParams p;
     std::memset(&p, 0, sizeof(p));
     p.n_split = 1;  // the kernels divide the grid by it: never 0
+    if (drop) {
+        p.drop_p = drop->p;
+        p.drop_scale = drop->p < 1.f ? 1.f / (1.f - drop->p) : 0.f;
+        p.seed_lo = (uint32_t)drop->seed;
+        p.seed_hi = (uint32_t)(drop->seed >> 32);
+        p.off_lo = (uint32_t)drop->offset;
+        p.off_hi = (uint32_t)(drop->offset >> 32);
+    }
     fa_strides s;
     if (strides) s = *strides;
     else std::memset(&s, 0, sizeof(s));
@@ -148,7 +169,7 @@ fa_status fa_fwd_strided(const void* Q, const void* K, const void* V, const void
     for (int a = 0; a < 3; ++a)
         if (s.mask[a] < 0) return fail(E, "fa_fwd: mask strides must be non-negative");
 
-    const fa::Variant* var = find_variant(dtype, D, mask_kind, causal);
+    const fa::Variant* var = find_variant(dtype, D, mask_kind, causal, drop != nullptr);
     if (!var)
         return fail(FA_ERR_UNSUPPORTED, "fa_fwd: no kernel built for dtype %d, D %d, mask %d, causal %d",
                     (int)dtype, D, (int)mask_kind, causal);
@@ -187,6 +208,34 @@ fa_status fa_fwd_strided(const void* Q, const void* K, const void* V, const void
     const hipError_t err = var->launch(p, (hipStream_t)hip_stream);
     if (err != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd: launch of %s failed: %s", var->name, hipGetErrorString(err));
     return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd_strided(const void* Q, const void* K, const void* V, const void* mask,
+                         void* O, float* L,
+                         int B, int H_q, int H_kv, int qL, int kL, int D,
+                         float scale, int causal,
+                         fa_dtype dtype, fa_mask_kind mask_kind,
+                         const fa_strides* strides, void* hip_stream)
+{
+    return fwd_impl(Q, K, V, mask, O, L, B, H_q, H_kv, qL, kL, D, scale, causal, dtype, mask_kind, strides,
+                    hip_stream, nullptr);
+}
+
+fa_status fa_fwd_dropout(const void* Q, const void* K, const void* V, const void* mask,
+                         void* O, float* L,
+                         int B, int H_q, int H_kv, int qL, int kL, int D,
+                         float scale, int causal,
+                         fa_dtype dtype, fa_mask_kind mask_kind,
+                         float p_drop, uint64_t seed, uint64_t offset,
+                         const fa_strides* strides, void* hip_stream)
+{
+    const DropArgs drop{p_drop, seed, offset};
+    return fwd_impl(Q, K, V, mask, O, L, B, H_q, H_kv, qL, kL, D, scale, causal, dtype, mask_kind, strides,
+                    hip_stream, &drop);
 }
 
 fa_status fa_fwd(const void* Q, const void* K, const void* V, const void* mask,

@@ -41,6 +41,13 @@ struct FwdParams {
     // Work-group kernel: rows [32 t, 32 t + 32) of NW query heads of one GQA
     // group per work-group, one head per wave (short query ranges).
     int head_pack;
+    // Dropout (the work-group kernel's dropout variants): a P V term is kept
+    // when the Philox-4x32-10 word drawn for its score position, as
+    // u = (word >> 8) / 2^24, is >= drop_p, and then scaled by drop_scale.
+    float drop_p;
+    float drop_scale;           // 1 / (1 - p), 0 when p >= 1
+    uint32_t seed_lo, seed_hi;  // the generator's key
+    uint32_t off_lo, off_hi;    // 64-bit offset added to every counter
 };
 
 enum MaskKind { MASK_NONE = 0, MASK_ADD = 1, MASK_BOOL = 2 };
@@ -117,5 +124,6 @@ struct Variant {
 // Variant tables defined by each kernel translation unit (host only).
 const Variant* variants_bf16(int* n);
 const Variant* variants_f32(int* n);
+const Variant* variants_bf16_dropout(int* n);
 
 }  // namespace fa

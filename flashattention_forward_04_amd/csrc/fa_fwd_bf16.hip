@@ -148,7 +148,38 @@ __device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
 //
 // K/V tiles are loaded straight from global memory into LDS (no registers),
 // round a ring of NB buffers, with one barrier per tile.
-template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB>
+// Philox-4x32 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel
+// random numbers: as easy as 1, 2, 3", SC 2011) on the counter (c0, c1, 0, 0)
+// under the key (k0, k1): each round multiplies words 0 and 2 by the round
+// constants, spreads the 64-bit products as (hi(c2 M1) ^ c1 ^ k0,
+// lo(c2 M1), hi(c0 M0) ^ c3 ^ k1, lo(c0 M0)) and advances the key by the
+// Weyl increments.
+struct Words4 {
+    uint32_t w0, w1, w2, w3;
+};
+__device__ __forceinline__ Words4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1)
+{
+    uint32_t c2 = 0u, c3 = 0u;
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+        const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return Words4{c0, c1, c2, c3};
+}
+__device__ __forceinline__ uint32_t word_at(const Words4& w, int i)
+{
+    return i == 0 ? w.w0 : i == 1 ? w.w1 : i == 2 ? w.w2 : w.w3;
+}
+
+template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB, bool DROP = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fwd_bf16_kernel(const FwdParams p)
 {
@@ -279,6 +310,33 @@ fwd_bf16_kernel(const FwdParams p)
     int t_last = n_tiles - 1;
     if (CAUSAL) t_last = min(t_last, (wq0 + 31) / BN - tb);
     if (wq0 >= p.qL || !head_ok) t_last = -1;
+
+    // dropout: the score position of this lane's row at key 0, and the
+    // dropout multipliers of the 4 consecutive keys from position n0
+    const int64_t drow = DROP ? (((int64_t)b * p.Hq + h) * p.qL + qrow) * p.kL : 0;
+    auto drop_quad = [&](int64_t n0, float* mult) __attribute__((always_inline)) {
+        const uint64_t off = ((uint64_t)p.off_hi << 32) | p.off_lo;
+        const uint64_t ctr = off + ((uint64_t)n0 >> 2);
+        const Words4 wa = philox4x32_10((uint32_t)ctr, (uint32_t)(ctr >> 32), p.seed_lo, p.seed_hi);
+        auto keep = [&](uint32_t w) __attribute__((always_inline)) {
+            return ((float)(w >> 8) * (1.f / 16777216.f) >= p.drop_p) ? p.drop_scale : 0.f;
+        };
+        if ((p.kL & 3) == 0) {
+            // every row starts at a multiple of 4: one block covers the quad
+            mult[0] = keep(wa.w0);
+            mult[1] = keep(wa.w1);
+            mult[2] = keep(wa.w2);
+            mult[3] = keep(wa.w3);
+        } else {
+            const Words4 wb = philox4x32_10((uint32_t)(ctr + 1), (uint32_t)((ctr + 1) >> 32), p.seed_lo, p.seed_hi);
+            const int sh = (int)(n0 & 3);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = sh + e;
+                mult[e] = keep(i < 4 ? word_at(wa, i) : word_at(wb, i - 4));
+            }
+        }
+    };
 
     // mask row of this lane (clamped so ragged rows read in bounds)
     const uint8_t* mrow = nullptr;
@@ -477,8 +535,8 @@ fwd_bf16_kernel(const FwdParams p)
     //             K operands of group r+2.
     // Stages are fenced (sched_barrier), and inside a stage the products and
     // vector instructions are issued alternately (sched_group_barrier).
-    auto softmax_pv = [&](f32x16 (&s)[NC], float cs, const uint16_t* vt, f32x16 (&sn)[NC], const uint16_t* kn)
-        __attribute__((always_inline)) {
+    auto softmax_pv = [&](f32x16 (&s)[NC], float cs, const uint16_t* vt, f32x16 (&sn)[NC], const uint16_t* kn,
+                          int j0) __attribute__((always_inline)) {
         constexpr int NCH = 2 * NC;                            // 16-key blocks per tile
         constexpr int NS = PIPE ? NP : 0;                      // next-tile score products
         constexpr int SS = PIPE ? (NP + NCH) / (NCH + 1) : 0;  // products per group
@@ -569,12 +627,24 @@ fwd_bf16_kernel(const FwdParams p)
             if (r + 1 <= NCH) s_mma(r + 1);
             if (r < NCH) {
                 const int c = r >> 1, hh = r & 1;
+                // dropout multipliers of this 16-key chunk: keys
+                // j0 + 32c + 8(2hh + qq) + 4g + {0..3}, qq = 0, 1
+                float mlt[8];
+                if constexpr (DROP) {
+                    drop_quad(drow + j0 + 32 * c + 16 * hh + 4 * g, mlt);
+                    drop_quad(drow + j0 + 32 * c + 16 * hh + 8 + 4 * g, mlt + 4);
+                }
                 u32x4 pw;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][8 * hh + 2 * e], cs, -m_use));
                     const float z = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][8 * hh + 2 * e + 1], cs, -m_use));
-                    pw[e] = pack_bf16x2(a, z);
+                    // the row sum takes P before dropout (l and L are those
+                    // without it); only the P V product sees the multipliers
+                    if constexpr (DROP)
+                        pw[e] = pack_bf16x2(a * mlt[4 * (e >> 1) + 2 * (e & 1)], z * mlt[4 * (e >> 1) + 2 * (e & 1) + 1]);
+                    else
+                        pw[e] = pack_bf16x2(a, z);
                     rs0 += a;
                     rs1 += z;
                 }
@@ -607,7 +677,7 @@ fwd_bf16_kernel(const FwdParams p)
         // softmax would make the register allocator move them at the join)
         if (masked) apply_mask(s, j0, mw);
         const float cs = masked ? 1.f : c2;
-        softmax_pv(s, cs, vt, sn, kn);
+        softmax_pv(s, cs, vt, sn, kn, j0);
     };
 
     f32x16 sa[NC], sb[NC];  // score tiles (two, for the pipelined schedule)
@@ -826,7 +896,7 @@ int split_plan(const FwdParams& p, int64_t wgs, int wgs_per_cu_, int* split_tile
     return (n_kt + st - 1) / st;
 }
 
-template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB>
+template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB, bool DROP = false>
 hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
 {
     constexpr int kWgsPerCu = wgs_per_cu<D, NW, BN, WPE, NB>();
@@ -837,7 +907,7 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
     const int n_split = split_plan<CAUSAL, BN, NB>(p, wgs, kWgsPerCu, &split_tiles);
     if (n_split < 2) {
         q.pair_tiles = CAUSAL && grid_fits_at_once(wgs, kWgsPerCu);
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB>), dim3((unsigned)wgs),
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB, DROP>), dim3((unsigned)wgs),
                            dim3(NW * 64), 0, st, q);
         return hipGetLastError();
     }
@@ -854,7 +924,7 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
     q.n_split = n_split;
     q.split_tiles = split_tiles;
     q.pair_tiles = CAUSAL && grid_fits_at_once(wgs * n_split, kWgsPerCu);
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB>), dim3((unsigned)(wgs * n_split)),
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB, DROP>), dim3((unsigned)(wgs * n_split)),
                        dim3(NW * 64), 0, st, q);
     err = hipGetLastError();
     if (err == hipSuccess) {
@@ -1526,6 +1596,29 @@ const Variant* variants_bf16(int* n)
     FA_BF16_FOR_D(96, FA_BF16_D96_CFG, FA_BF16_D96_MASKED_CFG),
     FA_BF16_FOR_D(128, FA_BF16_D128_CFG, FA_BF16_D128_MASKED_CFG),
     FA_BF16_FOR_D(256, FA_BF16_D256_CFG, FA_BF16_D256_MASKED_CFG),
+};
+    *n = (int)(sizeof(table) / sizeof(table[0]));
+    return table;
+}
+
+// Dropout variants: the work-group kernel at the head dims' own launch
+// shapes (no short-key or short-query special cases).
+#define FA_BF16_DROP_VARIANT(D, MASK, CAUSAL, NAME, NW, BN, WPE, SCHED, NB) \
+    {NAME, 1, D, MASK, CAUSAL, NW * 32, &launch_bf16<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB, true>}
+#define FA_BF16_DROP_VARIANT_CFG(...) FA_BF16_DROP_VARIANT(__VA_ARGS__)
+#define FA_BF16_DROP_FOR_D(D, CFG, MCFG)                                                           \
+    FA_BF16_DROP_VARIANT_CFG(D, MASK_NONE, false, "fwd_bf16_d" #D "_nomask_dropout", CFG),         \
+    FA_BF16_DROP_VARIANT_CFG(D, MASK_NONE, true, "fwd_bf16_d" #D "_nomask_causal_dropout", CFG),   \
+    FA_BF16_DROP_VARIANT_CFG(D, MASK_ADD, false, "fwd_bf16_d" #D "_additive_dropout", MCFG),       \
+    FA_BF16_DROP_VARIANT_CFG(D, MASK_ADD, true, "fwd_bf16_d" #D "_additive_causal_dropout", MCFG), \
+    FA_BF16_DROP_VARIANT_CFG(D, MASK_BOOL, false, "fwd_bf16_d" #D "_bool_dropout", MCFG),          \
+    FA_BF16_DROP_VARIANT_CFG(D, MASK_BOOL, true, "fwd_bf16_d" #D "_bool_causal_dropout", MCFG)
+
+const Variant* variants_bf16_dropout(int* n)
+{
+    static const Variant table[] = {
+    FA_BF16_DROP_FOR_D(64, FA_BF16_D64_CFG, FA_BF16_D64_MASKED_CFG),
+    FA_BF16_DROP_FOR_D(128, FA_BF16_D128_CFG, FA_BF16_D128_MASKED_CFG),
 };
     *n = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -118,6 +118,31 @@ fa_status fa_fwd_strided(const void* Q, const void* K, const void* V, const void
                          fa_dtype dtype, fa_mask_kind mask_kind,
                          const fa_strides* strides, void* hip_stream);
 
+/*
+ * fa_fwd_strided with dropout on the attention weights (ruDNN
+ * dense_attention.rs: `keep`, `keep_global` and the dropout branch of
+ * `forward_flash`).  Each allowed term of the P V sum is multiplied by
+ * k_ij / (1 - p_drop); the softmax denominator, and so L, are those
+ * without dropout.  k_ij = 1 when u_ij >= p_drop (never when p_drop = 1),
+ * where u_ij = floor(w / 2^8) / 2^24 and w is word (n mod 4) of
+ * Philox-4x32-10 (Salmon et al., SC 2011) applied to the 128-bit counter
+ * (offset + floor(n / 4) as a 64-bit value, low word first, then two zero
+ * words) under the key (seed low word, seed high word), for the score
+ * position n = ((b * H_q + h) * qL + i) * kL + j.  The same (seed, offset)
+ * reproduces the same mask; a caller drawing several masks advances offset
+ * by ceil(B * H_q * qL * kL / 4) between calls.
+ * p_drop must lie in [0, 1] (else FA_ERR_INVALID_ARGUMENT).  Built for bf16
+ * at D = 64 and 128, every mask kind, causal or not; other combinations
+ * return FA_ERR_UNSUPPORTED.  Everything else as fa_fwd_strided.
+ */
+fa_status fa_fwd_dropout(const void* Q, const void* K, const void* V, const void* mask,
+                         void* O, float* L,
+                         int B, int H_q, int H_kv, int qL, int kL, int D,
+                         float scale, int causal,
+                         fa_dtype dtype, fa_mask_kind mask_kind,
+                         float p_drop, uint64_t seed, uint64_t offset,
+                         const fa_strides* strides, void* hip_stream);
+
 /* 1 if (dtype, D, mask_kind, causal) has a compiled kernel, else 0. */
 int fa_supported(fa_dtype dtype, int D, fa_mask_kind mask_kind, int causal);
 

@@ -16,6 +16,7 @@ import torch
 import flashattention_forward_04_amd as fa
 import workloads as W
 from gpu_util import TOL_L, TOL_O, assert_parity, dtype_name, max_err, run_gpu, run_oracle
+from oracle import attention_fwd
 
 pytestmark = pytest.mark.gpu
 
@@ -431,3 +432,59 @@ def test_short_query_ranges_pack_gqa_heads(Hq, Hkv, qL, kL, D, kind, causal):
     assert_parity(O, L, Oref, Lref, "bf16", f"pack Hq={Hq}/{Hkv} qL={qL} kL={kL} D={D} {kind} causal={causal}")
     if kind != "none":
         assert np.all(O[1, Hq - 1, qL - 1] == 0) and L[1, Hq - 1, qL - 1] == 0
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("p", [0.0, 0.25, 1.0])
+@pytest.mark.parametrize("B,Hq,Hkv,qL,kL,causal,kind", [
+    (1, 2, 1, 130, 256, False, "none"),
+    (2, 4, 2, 77, 203, True, "none"),
+    (1, 2, 2, 64, 150, False, "bool"),
+    (1, 4, 1, 16, 4096, False, "additive"),
+], ids=lambda x: str(x))
+def test_dropout_matches_the_oracle(D, p, B, Hq, Hkv, qL, kL, causal, kind):
+    """Dropout on the attention weights: the keep mask is drawn from the same
+    Philox-4x32-10 positions on both sides, so O matches element by element;
+    L is the one without dropout.  kL = 203 and 150 put rows at offsets that
+    are not multiples of 4 (two generator blocks per 4 keys); 16 rows over
+    4096 keys split the key range over work-groups."""
+    seed, offset = 0x9E3779B97F4A7C15, (1 << 33) + 5
+    print(f"[case] dropout p={p} B={B} Hq={Hq} Hkv={Hkv} qL={qL} kL={kL} D={D} mask={kind} causal={causal}",
+          flush=True)
+    q, k, v = _rand((B, Hq, qL, D), BF16, 61), _rand((B, Hkv, kL, D), BF16, 62), _rand((B, Hkv, kL, D), BF16, 63)
+    mask = None
+    if kind != "none":
+        rng = np.random.default_rng(64)
+        masked = W.draw_masked(rng, (B, Hq, qL, kL), 0.3)
+        if kind == "bool":
+            mask = torch.from_numpy((~masked).astype(np.uint8))
+        else:
+            m = rng.standard_normal(masked.shape).astype(np.float32)
+            m[masked] = -np.inf
+            mask = torch.from_numpy(m).to(BF16)
+    scale = 1 / math.sqrt(D)
+    dev = torch.device("cuda:0")
+    Od, Ld = fa.fwd(q.to(dev), k.to(dev), v.to(dev), mask=None if mask is None else mask.to(dev), causal=causal,
+                    scale=scale, dropout_p=p, seed=seed, offset=offset)
+    torch.cuda.synchronize()
+    Od, Ld = Od.double().cpu().numpy(), Ld.double().cpu().numpy()
+    kindname = "none" if mask is None else ("bool" if kind == "bool" else "additive")
+    m_np = None if mask is None else (mask.numpy() if kind == "bool" else mask.double().numpy())
+    Oref, Lref = attention_fwd(q.double().numpy(), k.double().numpy(), v.double().numpy(), scale=scale, causal=causal,
+                               mask=m_np, mask_kind=kindname, dropout_p=p, seed=seed, offset=offset)
+    _, Lplain = run_oracle(q, k, v, mask, causal=causal, scale=scale)
+    assert_parity(Od, Ld, Oref, Lref, "bf16", f"dropout p={p} qL={qL} kL={kL} D={D} {kind} causal={causal}")
+    assert np.max(np.abs(Ld - Lplain)) <= TOL_L
+    if p == 1.0:
+        assert np.all(Od == 0)
+
+
+def test_dropout_rejects_bad_rates_and_unbuilt_shapes():
+    dev = torch.device("cuda:0")
+    q = torch.zeros((1, 1, 8, 64), dtype=BF16, device=dev)
+    for bad in (-0.1, 1.5, float("nan")):
+        with pytest.raises(fa.FaError):
+            fa.fwd(q, q, q, dropout_p=bad)
+    q32 = torch.zeros((1, 1, 8, 32), dtype=BF16, device=dev)
+    with pytest.raises(fa.FaError):
+        fa.fwd(q32, q32, q32, dropout_p=0.1)
