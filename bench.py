@@ -199,7 +199,8 @@ def summarize(prof_dir, w, commands):
 
 
 def find_workload(W, name):
-    every = {x.name: x for x in (*W.CONFIGS.values(), *W.SHORT_KL, *W.HEAD_DIMS, *W.SPLIT_KV, *W.RAGGED)}
+    every = {x.name: x for x in (*W.CONFIGS.values(), *W.SHORT_KL, *W.HEAD_DIMS, *W.SPLIT_KV, *W.DROPOUT,
+                                 *W.RAGGED)}
     if name not in every:
         raise SystemExit(f"unknown workload {name!r}; known: {', '.join(sorted(every))}")
     return every[name]
@@ -251,7 +252,8 @@ def cpu_baseline(w, q, k, v, mask, target_s: float):
         keys = np.minimum(i + 1, w.kL) if w.causal else np.full(rows.shape, w.kL)
         flops = float(4.0 * w.D * keys.sum())
         t0 = time.perf_counter()
-        lib.fwd(qd, kd, vd, scale=w.scale, causal=w.causal, mask=md, mask_kind=kind, rows=rows)
+        lib.fwd(qd, kd, vd, scale=w.scale, causal=w.causal, mask=md, mask_kind=kind, rows=rows,
+                dropout_p=w.dropout_p, seed=w.seed)
         return time.perf_counter() - t0, flops, rows.size
 
     dt, _, n = run(256)
@@ -339,7 +341,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        fa.fwd(qd, kd, vd, mask=md, causal=w.causal, scale=w.scale, out=out, lse=lse, stream=stream)
+        fa.fwd(qd, kd, vd, mask=md, causal=w.causal, scale=w.scale, out=out, lse=lse, stream=stream,
+               dropout_p=w.dropout_p, seed=w.seed)
 
     for _ in range(args.warmup):
         step()
@@ -400,6 +403,7 @@ def main():
         "data": "synthetic (seeded N(0,1) Q/K/V)",
         "config": {"workload": w.name, "B": w.B, "H_q": w.Hq, "H_kv": w.Hkv, "qL": w.qL, "kL": w.kL, "D": w.D,
                    "causal": w.causal, "mask": w.mask_kind, "scale": w.scale,
+                   **({"dropout": w.dropout_p} if w.dropout_p is not None else {}),
                    "o_layout": "token-major" if w.token_major_out else "head-major",
                    "flop_per_step": flops},
         "mfma_peak_frac": round(achieved / peak, 4),

@@ -46,14 +46,25 @@ def test_ragged(w):
     _full_parity(w)
 
 
-@pytest.mark.parametrize("w,n_rows", [(W.C3, 1536), (W.C4, 768), *[(x, 768) for x in W.HEAD_DIMS]],
+@pytest.mark.parametrize("w,n_rows", [(W.C3, 1536), (W.C4, 768), *[(x, 768) for x in W.HEAD_DIMS + W.DROPOUT]],
                          ids=lambda x: getattr(x, "name", str(x)))
 def test_config_full_size_sampled(w, n_rows):
     """Full-size launch (the configuration the benchmark times); oracle on sampled rows."""
     q, k, v, mask = _draw(w)
-    O, L, raw = run_gpu(q, k, v, mask, causal=w.causal, scale=w.scale, token_major=w.token_major_out)
+    if w.dropout_p is None:
+        O, L, raw = run_gpu(q, k, v, mask, causal=w.causal, scale=w.scale, token_major=w.token_major_out)
+    else:
+        dev = torch.device("cuda:0")
+        raw, Lt = fa.fwd(q.to(dev), k.to(dev), v.to(dev), causal=w.causal, scale=w.scale, dropout_p=w.dropout_p,
+                         seed=w.seed)
+        torch.cuda.synchronize()
+        O, L = raw.double().cpu().numpy(), Lt.double().cpu().numpy()
     rows = W.sample_rows(w, n_rows)
-    Oref, Lref = run_oracle(q, k, v, mask, causal=w.causal, scale=w.scale, rows=rows)
+    if w.dropout_p is None:
+        Oref, Lref = run_oracle(q, k, v, mask, causal=w.causal, scale=w.scale, rows=rows)
+    else:
+        Oref, Lref = attention_fwd(q.double().numpy(), k.double().numpy(), v.double().numpy(), scale=w.scale,
+                                   causal=w.causal, rows=rows, dropout_p=w.dropout_p, seed=w.seed)
     D = w.D
     assert_parity(O.reshape(-1, D)[rows], L.reshape(-1)[rows], Oref, Lref, w.dtype, w.name + " sampled")
     # properties of every row: finite; O inside the per-(b, head) range of V;
@@ -63,7 +74,12 @@ def test_config_full_size_sampled(w, n_rows):
     vmin = v.double().amin(dim=2).repeat_interleave(grp, dim=1).numpy()[:, :, None, :]
     vmax = v.double().amax(dim=2).repeat_interleave(grp, dim=1).numpy()[:, :, None, :]
     slack = TOL_O[w.dtype]
-    assert np.all(O >= vmin - slack) and np.all(O <= vmax + slack), "O outside the range of V"
+    if w.dropout_p is None:
+        assert np.all(O >= vmin - slack) and np.all(O <= vmax + slack), "O outside the range of V"
+    else:
+        # the kept weights of a row sum to at most 1 / (1 - p)
+        vabs = np.maximum(np.abs(vmin), np.abs(vmax)) / (1 - w.dropout_p)
+        assert np.all(np.abs(O) <= vabs + slack), "O beyond max|V| / (1 - p)"
     qd, kd = q.double(), k.double().repeat_interleave(grp, dim=1)
     s0 = (qd * kd[:, :, :1, :]).sum(-1).numpy() * w.scale
     ub = w.scale * qd.norm(dim=-1).numpy() * kd.norm(dim=-1).amax(dim=2, keepdim=True).numpy() + math.log(w.kL)

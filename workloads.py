@@ -39,6 +39,7 @@ class Workload:
     p_masked: float = 0.0
     token_major_out: bool = False
     seed: int = 0
+    dropout_p: float | None = None  # dropout rate on the attention weights (seed = the workload seed)
     note: str = ""
 
     def flops(self) -> float:
@@ -91,6 +92,12 @@ HEAD_DIMS = [
 SPLIT_KV = [
     Workload("decode_bf16_d128_32k", "bf16", 1, 32, 8, 16, 32768, 128, 1 / math.sqrt(128), seed=60,
              note="16 query rows over 32768 keys, bf16 D=128 (K/V-read bound)"),
+]
+
+# The headline shape with dropout on the attention weights (rate 0.1).
+DROPOUT = [
+    Workload("causal_bf16_d128_8k_dropout", "bf16", 1, 32, 8, 8192, 8192, 128, 1 / math.sqrt(128), causal=True,
+             seed=70, dropout_p=0.1, note="long-context causal bf16 with dropout 0.1 on the attention weights"),
 ]
 
 # Ragged shapes that are not tile multiples (the configs above all are).
