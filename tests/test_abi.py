@@ -139,3 +139,29 @@ def test_missing_library_fails_loudly(tmp_path):
             b.load_library(str(tmp_path / "absent.so"))
     finally:
         b._lib = saved
+
+
+def _dropout_call(p_drop, **over):
+    a = dict(BASE, **over)
+    return fa.fa_fwd_dropout(a["Q"], a["K"], a["V"], a["mask"], a["O"], a["L"], a["B"], a["H_q"], a["H_kv"], a["qL"],
+                             a["kL"], a["D"], a["scale"], a["causal"], a["dtype"], a["mask_kind"], p_drop,
+                             2 ** 64 - 1, 2 ** 63, None, a["hip_stream"])
+
+
+@pytest.mark.parametrize("p_drop", [-0.01, 1.0001, float("nan"), float("inf")])
+def test_dropout_rejects_rates_outside_0_1(lib, p_drop):
+    assert _dropout_call(p_drop) == fa.FA_ERR_INVALID_ARGUMENT
+    assert "dropout rate" in fa.fa_last_error()
+
+
+@pytest.mark.parametrize("over", [dict(dtype=fa.FA_DTYPE_F32), dict(D=32), dict(D=256)],
+                         ids=["f32", "d32", "d256"])
+def test_dropout_reports_unbuilt_combinations(lib, over):
+    # valid arguments, but no dropout kernel for the combination: nothing is launched
+    assert _dropout_call(0.1, **over) == fa.FA_ERR_UNSUPPORTED
+    assert "no kernel" in fa.fa_last_error()
+
+
+def test_dropout_checks_the_plain_arguments_too(lib):
+    assert _dropout_call(0.1, H_q=3) == fa.FA_ERR_INVALID_ARGUMENT
+    assert "divisible" in fa.fa_last_error()

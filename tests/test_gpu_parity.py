@@ -504,3 +504,14 @@ def test_dropout_rejects_bad_rates_and_unbuilt_shapes():
     q32 = torch.zeros((1, 1, 8, 32), dtype=BF16, device=dev)
     with pytest.raises(fa.FaError):
         fa.fwd(q32, q32, q32, dropout_p=0.1)
+
+
+def test_split_over_more_ranges_than_lanes():
+    """One query tile of one head over 65536 keys: the key range splits over
+    more work-groups than a wave has lanes (128 ranges), so the merge's
+    per-lane loops over the ranges take several turns."""
+    print("[case] split 1 head qL=16 kL=65536 D=128", flush=True)
+    q, k, v = _rand((1, 1, 16, 128), BF16, 71), _rand((1, 1, 65536, 128), BF16, 72), _rand((1, 1, 65536, 128), BF16, 73)
+    O, L, _ = run_gpu(q, k, v, scale=1 / math.sqrt(128))
+    Oref, Lref = run_oracle(q, k, v, scale=1 / math.sqrt(128))
+    assert_parity(O, L, Oref, Lref, "bf16", "split into 128 ranges")
