@@ -147,6 +147,10 @@ fa_status fwd_impl(const void* Q, const void* K, const void* V, const void* mask
     if (drop) {
         p.drop_p = drop->p;
         p.drop_scale = drop->p < 1.f ? 1.f / (1.f - drop->p) : 0.f;
+        // p 2^24 is exact in fp32 (a power-of-two scaling), so its ceiling is
+        // the smallest kept floor(w / 2^8); p = 1 wraps to 0 and is dropped
+        // through drop_scale = 0 instead
+        p.drop_thresh = (uint32_t)std::ceil((double)drop->p * 16777216.0) << 8;
         p.seed_lo = (uint32_t)drop->seed;
         p.seed_hi = (uint32_t)(drop->seed >> 32);
         p.off_lo = (uint32_t)drop->offset;

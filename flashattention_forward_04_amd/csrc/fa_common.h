@@ -46,6 +46,7 @@ struct FwdParams {
     // u = (word >> 8) / 2^24, is >= drop_p, and then scaled by drop_scale.
     float drop_p;
     float drop_scale;           // 1 / (1 - p), 0 when p >= 1
+    uint32_t drop_thresh;       // ceil(p 2^24) 2^8 (mod 2^32): keep iff the word is >= it
     uint32_t seed_lo, seed_hi;  // the generator's key
     uint32_t off_lo, off_hi;    // 64-bit offset added to every counter
 };

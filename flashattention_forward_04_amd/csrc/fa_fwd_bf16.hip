@@ -162,8 +162,11 @@ __device__ __forceinline__ Words4 philox4x32_10(uint32_t c0, uint32_t c1, uint32
     uint32_t c2 = 0u, c3 = 0u;
 #pragma unroll
     for (int round = 0; round < 10; ++round) {
-        const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+        // one 32 x 32 -> 64-bit product each (a single multiply-add
+        // instruction rather than separate low and high multiplies)
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
         const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
         c0 = n0;
         c1 = lo1;
@@ -318,8 +321,10 @@ fwd_bf16_kernel(const FwdParams p)
         const uint64_t off = ((uint64_t)p.off_hi << 32) | p.off_lo;
         const uint64_t ctr = off + ((uint64_t)n0 >> 2);
         const Words4 wa = philox4x32_10((uint32_t)ctr, (uint32_t)(ctr >> 32), p.seed_lo, p.seed_hi);
+        // u = floor(w / 2^8) / 2^24 >= p  <=>  floor(w / 2^8) >= ceil(p 2^24)
+        // <=>  w >= ceil(p 2^24) 2^8 = drop_thresh (an integer compare)
         auto keep = [&](uint32_t w) __attribute__((always_inline)) {
-            return ((float)(w >> 8) * (1.f / 16777216.f) >= p.drop_p) ? p.drop_scale : 0.f;
+            return (w >= p.drop_thresh) ? p.drop_scale : 0.f;
         };
         if ((p.kL & 3) == 0) {
             // every row starts at a multiple of 4: one block covers the quad
