@@ -30,6 +30,11 @@
  *     L[b,h,i]   = m_i + ln(l_i)                (natural-log logsumexp:
  *                  mlx-native flash_attn_train.rs, module doc "Algorithm")
  *
+ *   Sliding window (fa_oracle_fwd_window; the forge header's FlashParams
+ *   carries a `window` field that it routes elsewhere and never defines, so
+ *   this is a reading): with window W >= 1 and causal, key j is allowed only
+ *   when additionally i - j < W, i.e. row i sees keys i - W + 1 .. i.
+ *
  *   A row with no allowed key gets O = 0 and L = 0 (forge
  *   flash_attention_mma.metal, epilogue of flash_attn_fwd_mma: l = 0 writes
  *   zeros for both).
@@ -126,7 +131,7 @@ typedef struct {
 static void one_row(const double* Q, const double* K, const double* V,
                     const double* mask, int mask_kind,
                     int Hq, int Hkv, int qL, int kL, int D, double scale,
-                    int causal, int64_t flat, double* s, unsigned char* ok,
+                    int causal, int window, int64_t flat, double* s, unsigned char* ok,
                     double* o, double* lse, const dropout_t* drop)
 {
     const int64_t i = flat % qL;
@@ -148,6 +153,7 @@ static void one_row(const double* Q, const double* K, const double* V,
         double sc = scale * dot;
         int allowed = 1;
         if (causal && j > i) allowed = 0;
+        if (window > 0 && i - j >= window) allowed = 0;
         if (mask_kind == 1) sc = sc + mrow[j];
         if (mask_kind == 2 && mrow[j] == 0.0) allowed = 0;
         if (sc == -INFINITY) allowed = 0;
@@ -189,10 +195,11 @@ static void one_row(const double* Q, const double* K, const double* V,
 static int run_rows(const double* Q, const double* K, const double* V,
                     const double* mask, int mask_kind,
                     int B, int Hq, int Hkv, int qL, int kL, int D,
-                    double scale, int causal,
+                    double scale, int causal, int window,
                     const int64_t* rows, int64_t nrows,
                     double* O, double* L, const dropout_t* drop)
 {
+    if (window < 0 || (window > 0 && !causal)) return -1;
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || qL <= 0 || kL <= 0 || D <= 0) return -1;
     if (Hq % Hkv != 0) return -1;
     if (mask_kind < 0 || mask_kind > 2) return -1;
@@ -215,7 +222,7 @@ static int run_rows(const double* Q, const double* K, const double* V,
             for (int64_t r = 0; r < nrows; ++r) {
                 const int64_t flat = rows ? rows[r] : r;
                 one_row(Q, K, V, mask, mask_kind, Hq, Hkv, qL, kL, D, scale,
-                        causal, flat, s, ok, O + r * D, L + r, drop);
+                        causal, window, flat, s, ok, O + r * D, L + r, drop);
             }
         }
         free(s);
@@ -232,7 +239,22 @@ int fa_oracle_fwd(const double* Q, const double* K, const double* V,
                   double* O, double* L)
 {
     const dropout_t none = {0, 0.0f, 0, 0};
-    return run_rows(Q, K, V, mask, mask_kind, B, Hq, Hkv, qL, kL, D, scale, causal, rows, nrows, O, L, &none);
+    return run_rows(Q, K, V, mask, mask_kind, B, Hq, Hkv, qL, kL, D, scale, causal, 0, rows, nrows, O, L, &none);
+}
+
+/* fa_oracle_fwd restricted to a causal sliding window of `window` >= 1 keys
+ * (see the header); returns -1 unless causal. */
+int fa_oracle_fwd_window(const double* Q, const double* K, const double* V,
+                         const double* mask, int mask_kind,
+                         int B, int Hq, int Hkv, int qL, int kL, int D,
+                         double scale, int causal,
+                         const int64_t* rows, int64_t nrows,
+                         double* O, double* L, int window)
+{
+    if (window < 1) return -1;
+    const dropout_t none = {0, 0.0f, 0, 0};
+    return run_rows(Q, K, V, mask, mask_kind, B, Hq, Hkv, qL, kL, D, scale, causal, window, rows, nrows, O, L,
+                    &none);
 }
 
 /* fa_oracle_fwd with dropout of rate p (0 <= p <= 1) under `seed` and
@@ -247,5 +269,5 @@ int fa_oracle_fwd_dropout(const double* Q, const double* K, const double* V,
 {
     if (!(p >= 0.0f && p <= 1.0f)) return -1;
     const dropout_t drop = {1, p, seed, offset};
-    return run_rows(Q, K, V, mask, mask_kind, B, Hq, Hkv, qL, kL, D, scale, causal, rows, nrows, O, L, &drop);
+    return run_rows(Q, K, V, mask, mask_kind, B, Hq, Hkv, qL, kL, D, scale, causal, 0, rows, nrows, O, L, &drop);
 }

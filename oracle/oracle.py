@@ -47,6 +47,9 @@ class OracleLib:
         fd = self.lib.fa_oracle_fwd_dropout
         fd.argtypes = list(f.argtypes) + [ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64]
         fd.restype = ctypes.c_int
+        fw = self.lib.fa_oracle_fwd_window
+        fw.argtypes = list(f.argtypes) + [ctypes.c_int]
+        fw.restype = ctypes.c_int
         u32p = ctypes.POINTER(ctypes.c_uint32)
         self.lib.fa_oracle_philox4x32_10.argtypes = [u32p, u32p, u32p]
         self.lib.fa_oracle_philox4x32_10.restype = None
@@ -71,13 +74,14 @@ class OracleLib:
         return float(self.lib.fa_oracle_dropout_multiplier(int(n), float(p), int(seed), int(offset)))
 
     def fwd(self, q, k, v, *, scale, causal=False, mask=None, mask_kind="none", rows=None,
-            dropout_p=None, seed=0, offset=0):
+            dropout_p=None, seed=0, offset=0, window=None):
         """Attention forward in fp64.
 
         q [B,Hq,qL,D], k/v [B,Hkv,kL,D]; mask broadcastable to [B,Hq,qL,kL]
         (additive values, or bool/uint8 with nonzero = attend).
         Returns (O, L): O [B,Hq,qL,D] and L [B,Hq,qL], or O [n,D] and L [n]
         for the flat row indices `rows` (flat = (b*Hq + h)*qL + i).
+        window (causal only): row i sees keys i - window + 1 .. i.
         """
         q = np.ascontiguousarray(q, dtype=np.float64)
         k = np.ascontiguousarray(k, dtype=np.float64)
@@ -111,7 +115,11 @@ class OracleLib:
         args = (q.ctypes.data_as(dp), k.ctypes.data_as(dp), v.ctypes.data_as(dp),
                 mptr, kind, B, Hq, Hkv, qL, kL, D, float(scale), int(bool(causal)),
                 rptr, n, O.ctypes.data_as(dp), L.ctypes.data_as(dp))
-        if dropout_p is None:
+        if window is not None and dropout_p is not None:
+            raise ValueError("oracle: window and dropout are not combined")
+        if window is not None:
+            rc = self.lib.fa_oracle_fwd_window(*args, int(window))
+        elif dropout_p is None:
             rc = self.lib.fa_oracle_fwd(*args)
         else:
             rc = self.lib.fa_oracle_fwd_dropout(*args, float(dropout_p), int(seed), int(offset))
@@ -133,11 +141,12 @@ def _default() -> OracleLib:
 
 
 def attention_fwd(q, k, v, *, scale, causal=False, mask=None, mask_kind="none", rows=None,
-                  dropout_p=None, seed=0, offset=0):
+                  dropout_p=None, seed=0, offset=0, window=None):
     """fp64 attention forward with the default compiled oracle (see OracleLib.fwd).  With
-    dropout_p set, each P V term is scaled by its keep decision / (1 - p) (L is unchanged)."""
+    dropout_p set, each P V term is scaled by its keep decision / (1 - p) (L is unchanged);
+    with window set (causal only), row i sees keys i - window + 1 .. i."""
     return _default().fwd(q, k, v, scale=scale, causal=causal, mask=mask, mask_kind=mask_kind, rows=rows,
-                          dropout_p=dropout_p, seed=seed, offset=offset)
+                          dropout_p=dropout_p, seed=seed, offset=offset, window=window)
 
 
 def philox4x32_10(ctr, key):
