@@ -200,7 +200,7 @@ def summarize(prof_dir, w, commands):
 
 def find_workload(W, name):
     every = {x.name: x for x in (*W.CONFIGS.values(), *W.SHORT_KL, *W.HEAD_DIMS, *W.SPLIT_KV, *W.DROPOUT,
-                                 *W.RAGGED)}
+                                 *W.WINDOW, *W.RAGGED)}
     if name not in every:
         raise SystemExit(f"unknown workload {name!r}; known: {', '.join(sorted(every))}")
     return every[name]
@@ -250,10 +250,12 @@ def cpu_baseline(w, q, k, v, mask, target_s: float):
         rows = np.sort(rng.choice(total_rows, size=min(n, total_rows), replace=False)).astype(np.int64)
         i = rows % w.qL
         keys = np.minimum(i + 1, w.kL) if w.causal else np.full(rows.shape, w.kL)
+        if w.window is not None:
+            keys = np.maximum(0, keys - np.maximum(0, i - w.window + 1))
         flops = float(4.0 * w.D * keys.sum())
         t0 = time.perf_counter()
         lib.fwd(qd, kd, vd, scale=w.scale, causal=w.causal, mask=md, mask_kind=kind, rows=rows,
-                dropout_p=w.dropout_p, seed=w.seed)
+                dropout_p=w.dropout_p, seed=w.seed, window=w.window)
         return time.perf_counter() - t0, flops, rows.size
 
     dt, _, n = run(256)
@@ -342,7 +344,7 @@ def main():
 
     def step():
         fa.fwd(qd, kd, vd, mask=md, causal=w.causal, scale=w.scale, out=out, lse=lse, stream=stream,
-               dropout_p=w.dropout_p, seed=w.seed)
+               dropout_p=w.dropout_p, seed=w.seed, window=w.window)
 
     for _ in range(args.warmup):
         step()
@@ -404,6 +406,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H_q": w.Hq, "H_kv": w.Hkv, "qL": w.qL, "kL": w.kL, "D": w.D,
                    "causal": w.causal, "mask": w.mask_kind, "scale": w.scale,
                    **({"dropout": w.dropout_p} if w.dropout_p is not None else {}),
+                   **({"window": w.window} if w.window is not None else {}),
                    "o_layout": "token-major" if w.token_major_out else "head-major",
                    "flop_per_step": flops},
         "mfma_peak_frac": round(achieved / peak, 4),

@@ -18,7 +18,7 @@ FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_DTYPE_F32, FA_DTYPE_BF16 = 0, 1
 FA_MASK_NONE, FA_MASK_ADDITIVE, FA_MASK_BOOL = 0, 1, 2
 
-EXPORTS = ("fa_fwd", "fa_fwd_strided", "fa_fwd_dropout", "fa_supported", "fa_variant_count", "fa_variant_name",
+EXPORTS = ("fa_fwd", "fa_fwd_strided", "fa_fwd_dropout", "fa_fwd_window", "fa_supported", "fa_variant_count", "fa_variant_name",
            "fa_status_string", "fa_last_error", "fa_abi_version")
 
 
@@ -56,6 +56,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, i32, f32,
                                    ctypes.c_uint64, ctypes.c_uint64, ctypes.POINTER(FaStrides), vp]
     lib.fa_fwd_dropout.restype = i32
+    lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, i32, i32,
+                                  ctypes.POINTER(FaStrides), vp]
+    lib.fa_fwd_window.restype = i32
     lib.fa_supported.argtypes = [i32, i32, i32, i32]
     lib.fa_supported.restype = i32
     lib.fa_variant_count.restype = i32
@@ -81,6 +84,13 @@ def fa_fwd_dropout(Q, K, V, mask, O, L, B, H_q, H_kv, qL, kL, D, scale, causal, 
     ref = ctypes.byref(strides) if strides is not None else None
     return load_library().fa_fwd_dropout(Q, K, V, mask, O, L, B, H_q, H_kv, qL, kL, D, scale, causal, dtype,
                                          mask_kind, p_drop, seed, offset, ref, hip_stream)
+
+
+def fa_fwd_window(Q, K, V, mask, O, L, B, H_q, H_kv, qL, kL, D, scale, causal, dtype, mask_kind, window, strides,
+                  hip_stream) -> int:
+    ref = ctypes.byref(strides) if strides is not None else None
+    return load_library().fa_fwd_window(Q, K, V, mask, O, L, B, H_q, H_kv, qL, kL, D, scale, causal, dtype,
+                                        mask_kind, window, ref, hip_stream)
 
 
 def fa_fwd_strided(Q, K, V, mask, O, L, B, H_q, H_kv, qL, kL, D, scale, causal, dtype, mask_kind, strides,
@@ -136,7 +146,7 @@ def _check_extent(t, shape, strides, name):
 
 
 def fwd(q, k, v, *, mask=None, causal=False, scale=None, out=None, lse=None, stream=None, dropout_p=None, seed=0,
-        offset=0):
+        offset=0, window=None):
     """O, L = attention forward on the GPU through libfa_mi355x.
 
     q [B, H_q, qL, D]; k, v [B, H_kv, kL, D]: bf16 or fp32 CUDA tensors whose
@@ -152,6 +162,8 @@ def fwd(q, k, v, *, mask=None, causal=False, scale=None, out=None, lse=None, str
     dropout_p: None, or a rate in [0, 1] for dropout on the attention weights
     under the 64-bit `seed` and counter `offset` (fa_fwd_dropout; bf16 at
     D = 64 and 128).
+    window: None, or a causal sliding window of that many keys (row i sees
+    keys i - window + 1 .. i; fa_fwd_window, bf16, causal only).
     """
     import torch
 
@@ -222,7 +234,13 @@ def fwd(q, k, v, *, mask=None, causal=False, scale=None, out=None, lse=None, str
 
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    if dropout_p is None:
+    if window is not None and dropout_p is not None:
+        raise ValueError("fa: window and dropout_p are not combined")
+    if window is not None:
+        check(fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, out.data_ptr(), lse.data_ptr(),
+                            B, Hq, Hkv, qL, kL, D, float(scale), int(bool(causal)), dtype, mask_kind, int(window),
+                            st, stream.cuda_stream))
+    elif dropout_p is None:
         check(fa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, out.data_ptr(), lse.data_ptr(),
                              B, Hq, Hkv, qL, kL, D, float(scale), int(bool(causal)), dtype, mask_kind, st,
                              stream.cuda_stream))

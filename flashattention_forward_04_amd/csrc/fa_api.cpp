@@ -113,7 +113,7 @@ fa_status fwd_impl(const void* Q, const void* K, const void* V, const void* mask
                    int B, int H_q, int H_kv, int qL, int kL, int D,
                    float scale, int causal,
                    fa_dtype dtype, fa_mask_kind mask_kind,
-                   const fa_strides* strides, void* hip_stream, const DropArgs* drop)
+                   const fa_strides* strides, void* hip_stream, const DropArgs* drop, int window = 0)
 {
     g_last_error[0] = '\0';
     const fa_status E = FA_ERR_INVALID_ARGUMENT;
@@ -134,6 +134,8 @@ fa_status fwd_impl(const void* Q, const void* K, const void* V, const void* mask
     if (!std::isfinite(scale)) return fail(E, "fa_fwd: scale must be finite");
     if (drop && !(drop->p >= 0.f && drop->p <= 1.f))
         return fail(E, "fa_fwd_dropout: the dropout rate must lie in [0, 1], got %g", (double)drop->p);
+    if (window < 0) return fail(E, "fa_fwd_window: the window must be >= 1 key, got %d", window);
+    if (window > 0 && !causal) return fail(E, "fa_fwd_window: a sliding window needs causal = 1");
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(L, 4))
         return fail(E, "fa_fwd: Q, K, V and O must be 16-byte aligned and L 4-byte aligned");
     if ((int64_t)B * H_q * qL * D > INT64_MAX / 8 || (int64_t)B * H_q * qL * kL > INT64_MAX / 8)
@@ -144,6 +146,7 @@ fa_status fwd_impl(const void* Q, const void* K, const void* V, const void* mask
     fa::FwdParams p;
     std::memset(&p, 0, sizeof(p));
     p.n_split = 1;  // the kernels divide the grid by it: never 0
+    p.window = window;
     if (drop) {
         p.drop_p = drop->p;
         p.drop_scale = drop->p < 1.f ? 1.f / (1.f - drop->p) : 0.f;
@@ -174,6 +177,8 @@ fa_status fwd_impl(const void* Q, const void* K, const void* V, const void* mask
         if (s.mask[a] < 0) return fail(E, "fa_fwd: mask strides must be non-negative");
 
     const fa::Variant* var = find_variant(dtype, D, mask_kind, causal, drop != nullptr);
+    if (window > 0 && dtype != FA_DTYPE_BF16)
+        return fail(FA_ERR_UNSUPPORTED, "fa_fwd_window: no kernel built for a sliding window in dtype %d", (int)dtype);
     if (!var)
         return fail(FA_ERR_UNSUPPORTED, "fa_fwd: no kernel built for dtype %d, D %d, mask %d, causal %d",
                     (int)dtype, D, (int)mask_kind, causal);
@@ -240,6 +245,21 @@ fa_status fa_fwd_dropout(const void* Q, const void* K, const void* V, const void
     const DropArgs drop{p_drop, seed, offset};
     return fwd_impl(Q, K, V, mask, O, L, B, H_q, H_kv, qL, kL, D, scale, causal, dtype, mask_kind, strides,
                     hip_stream, &drop);
+}
+
+fa_status fa_fwd_window(const void* Q, const void* K, const void* V, const void* mask,
+                        void* O, float* L,
+                        int B, int H_q, int H_kv, int qL, int kL, int D,
+                        float scale, int causal,
+                        fa_dtype dtype, fa_mask_kind mask_kind,
+                        int window, const fa_strides* strides, void* hip_stream)
+{
+    if (window < 1) {
+        g_last_error[0] = '\0';
+        return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd_window: the window must be >= 1 key, got %d", window);
+    }
+    return fwd_impl(Q, K, V, mask, O, L, B, H_q, H_kv, qL, kL, D, scale, causal, dtype, mask_kind, strides,
+                    hip_stream, nullptr, window);
 }
 
 fa_status fa_fwd(const void* Q, const void* K, const void* V, const void* mask,

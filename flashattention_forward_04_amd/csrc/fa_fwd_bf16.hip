@@ -305,9 +305,11 @@ fwd_bf16_kernel(const FwdParams p)
     const float c2 = p.scale_log2;
     const int kv_end = CAUSAL ? min(p.kL, min(p.qL, q0 + (p.head_pack ? 32 : BM))) : p.kL;
     // key tiles of this query tile; a split work-group takes tiles
-    // [tb, tb + split_tiles) of them, numbered from 0 below
+    // [tb, tb + split_tiles) of them, numbered from 0 below.  A sliding
+    // window starts the range at the tile of the first row's first key.
+    const bool win = CAUSAL && p.window > 0;
     const int n_all = (kv_end + BN - 1) / BN;
-    const int tb = split * p.split_tiles;
+    const int tb = (win ? max(0, q0 - p.window + 1) / BN : 0) + split * p.split_tiles;
     const int n_tiles = max(0, (p.n_split > 1 ? min(n_all, tb + p.split_tiles) : n_all) - tb);
     // this wave needs tiles 0..t_last (a prefix: causal rows never see later keys)
     int t_last = n_tiles - 1;
@@ -491,11 +493,25 @@ fwd_bf16_kernel(const FwdParams p)
     // ---- scores of key tile j0 -> base 2, excluded keys at -inf: keys past
     // kL, keys after the row (causal), and the user mask (its words in mw) ----
     auto apply_mask = [&](f32x16 (&s)[NC], int j0, const MaskWords& mw) __attribute__((always_inline)) {
+        // the tile reaches below the window of the wave's last row
+        const bool w_edge = win && j0 < wq0 + 32 - p.window;
         if (MASK == MASK_NONE) {
             // key j0 + 32c + 8rq + 4g + e is allowed iff 32c + 8rq + e <= lim
+            // (and, on a window's edge, >= lo)
             int lim = p.kL - 1;
             if (CAUSAL) lim = min(lim, qrow);
             lim -= j0 + 4 * g;
+            if (w_edge) {
+                const int lo = qrow - p.window + 1 - (j0 + 4 * g);
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int x = 32 * c + 8 * (r >> 2) + (r & 3);
+                        s[c][r] = (x <= lim && x >= lo) ? s[c][r] * c2 : -INFINITY;
+                    }
+                return;
+            }
 #pragma unroll
             for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -515,6 +531,7 @@ fwd_bf16_kernel(const FwdParams p)
                     bool ok = j < p.kL;
                     if (MASK == MASK_BOOL) ok = ok && ((w[0] >> (8 * e)) & 0xffu) != 0;
                     if (CAUSAL) ok = ok && (j <= qrow);
+                    if (CAUSAL) ok = ok && (!w_edge || j > qrow - p.window);
                     float x = s[c][4 * rq + e] * c2;
                     if (MASK == MASK_ADD) {
                         const uint32_t bits = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
@@ -676,7 +693,9 @@ fwd_bf16_kernel(const FwdParams p)
     auto finish_tile = [&](int t, f32x16 (&s)[NC], const uint16_t* vt, f32x16 (&sn)[NC], const uint16_t* kn,
                            const MaskWords& mw) __attribute__((always_inline)) {
         const int j0 = (tb + t) * BN;
-        const bool masked = (MASK != MASK_NONE) || (j0 + BN > p.kL) || (CAUSAL && j0 + BN - 1 > wq0);
+        // (a window's left edge: the wave's last row starts at key wq0 + 32 - window)
+        const bool masked = (MASK != MASK_NONE) || (j0 + BN > p.kL) || (CAUSAL && j0 + BN - 1 > wq0) ||
+                            (win && j0 < wq0 + 32 - p.window);
         // one softmax for both kinds of tile, so that the accumulators and
         // the next tile's scores are written in one place (two copies of the
         // softmax would make the register allocator move them at the join)
@@ -890,7 +909,7 @@ int split_plan(const FwdParams& p, int64_t wgs, int wgs_per_cu_, int* split_tile
     const int kv_max = CAUSAL ? min(p.kL, p.qL) : p.kL;
     const int n_kt = (kv_max + BN - 1) / BN;
     *split_tiles = 0;
-    if (!FA_SPLIT_KV || wgs * 2 > kCUs || n_kt < 2 * kMinSplitTiles) return 1;
+    if (!FA_SPLIT_KV || p.window > 0 || wgs * 2 > kCUs || n_kt < 2 * kMinSplitTiles) return 1;
     const int64_t want = (int64_t)kCUs * wgs_per_cu_ / wgs;
     const int by_len = n_kt / kMinSplitTiles;
     const int s0 = (int)(want < by_len ? want : (int64_t)by_len);
@@ -1461,7 +1480,7 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
     if (p.n_split < 1) return hipErrorInvalidValue;
     if constexpr (D == 128) {
         // Short key ranges are HBM-bound (Q in, O out).
-        if (MASK == MASK_NONE && p.kL <= 4 * 32) {
+        if (MASK == MASK_NONE && p.kL <= 4 * 32 && p.window == 0) {
             // streaming kernel: enough work-groups per kv head to fill the
             // GPU twice over, each with at least a few query blocks per wave
             constexpr int kResident = 2 * 256;
@@ -1496,7 +1515,7 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
         // 1024 rows x 3072 keys), else over the waves of one work-group.
         constexpr int kCUs = 256;
         int split_tiles = 0;
-        if ((int64_t)p.n_qtiles * p.Hq * p.B < kCUs &&
+        if (p.window == 0 && (int64_t)p.n_qtiles * p.Hq * p.B < kCUs &&
             split_plan<CAUSAL, BN, NB>(p, (int64_t)p.n_qtiles * p.Hq * p.B, wgs_per_cu<D, NW, BN, WPE, NB>(),
                                        &split_tiles) < 2) {
             FwdParams q = p;

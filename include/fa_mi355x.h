@@ -143,6 +143,26 @@ fa_status fa_fwd_dropout(const void* Q, const void* K, const void* V, const void
                          float p_drop, uint64_t seed, uint64_t offset,
                          const fa_strides* strides, void* hip_stream);
 
+/*
+ * fa_fwd_strided restricted to a causal sliding window: query row i attends
+ * to keys i - window + 1 .. i (and within them to what the mask allows).
+ * The forge flash_attention_mma.metal header carries a `window` field in
+ * FlashParams that it routes to kernels it does not show and never defines;
+ * this causal-window meaning is the reading taken here.  window >= kL (more
+ * generally, >= qL) is plain causal attention.  A row left with no key gets
+ * O = 0 and L = 0, as in fa_fwd.
+ * window must be >= 1 and causal must be 1 (else FA_ERR_INVALID_ARGUMENT).
+ * Built for bf16 at every D and mask kind; fp32 returns FA_ERR_UNSUPPORTED.
+ * A windowed launch never splits its key range over work-groups, so it
+ * allocates nothing.  Everything else as fa_fwd_strided.
+ */
+fa_status fa_fwd_window(const void* Q, const void* K, const void* V, const void* mask,
+                        void* O, float* L,
+                        int B, int H_q, int H_kv, int qL, int kL, int D,
+                        float scale, int causal,
+                        fa_dtype dtype, fa_mask_kind mask_kind,
+                        int window, const fa_strides* strides, void* hip_stream);
+
 /* 1 if (dtype, D, mask_kind, causal) has a compiled kernel, else 0. */
 int fa_supported(fa_dtype dtype, int D, fa_mask_kind mask_kind, int causal);
 

@@ -165,3 +165,31 @@ def test_dropout_reports_unbuilt_combinations(lib, over):
 def test_dropout_checks_the_plain_arguments_too(lib):
     assert _dropout_call(0.1, H_q=3) == fa.FA_ERR_INVALID_ARGUMENT
     assert "divisible" in fa.fa_last_error()
+
+
+def _window_call(window, **over):
+    a = dict(BASE, **dict(dict(causal=1), **over))
+    return fa.fa_fwd_window(a["Q"], a["K"], a["V"], a["mask"], a["O"], a["L"], a["B"], a["H_q"], a["H_kv"], a["qL"],
+                            a["kL"], a["D"], a["scale"], a["causal"], a["dtype"], a["mask_kind"], window, None,
+                            a["hip_stream"])
+
+
+@pytest.mark.parametrize("window", [0, -1, -(2 ** 31)])
+def test_window_rejects_widths_below_one(lib, window):
+    assert _window_call(window) == fa.FA_ERR_INVALID_ARGUMENT
+    assert "window must be >= 1" in fa.fa_last_error()
+
+
+def test_window_needs_causal(lib):
+    assert _window_call(16, causal=0) == fa.FA_ERR_INVALID_ARGUMENT
+    assert "needs causal" in fa.fa_last_error()
+
+
+def test_window_reports_fp32_as_unbuilt(lib):
+    assert _window_call(16, dtype=fa.FA_DTYPE_F32) == fa.FA_ERR_UNSUPPORTED
+    assert "sliding window" in fa.fa_last_error()
+
+
+def test_window_checks_the_plain_arguments_too(lib):
+    assert _window_call(16, H_q=3) == fa.FA_ERR_INVALID_ARGUMENT
+    assert "divisible" in fa.fa_last_error()

@@ -46,29 +46,31 @@ def test_ragged(w):
     _full_parity(w)
 
 
-@pytest.mark.parametrize("w,n_rows", [(W.C3, 1536), (W.C4, 768), *[(x, 768) for x in W.HEAD_DIMS + W.DROPOUT]],
+@pytest.mark.parametrize("w,n_rows", [(W.C3, 1536), (W.C4, 768),
+                                       *[(x, 768) for x in W.HEAD_DIMS + W.DROPOUT + W.WINDOW]],
                          ids=lambda x: getattr(x, "name", str(x)))
 def test_config_full_size_sampled(w, n_rows):
     """Full-size launch (the configuration the benchmark times); oracle on sampled rows."""
     q, k, v, mask = _draw(w)
-    if w.dropout_p is None:
+    if w.dropout_p is None and w.window is None:
         O, L, raw = run_gpu(q, k, v, mask, causal=w.causal, scale=w.scale, token_major=w.token_major_out)
     else:
         dev = torch.device("cuda:0")
         raw, Lt = fa.fwd(q.to(dev), k.to(dev), v.to(dev), causal=w.causal, scale=w.scale, dropout_p=w.dropout_p,
-                         seed=w.seed)
+                         seed=w.seed, window=w.window)
         torch.cuda.synchronize()
         O, L = raw.double().cpu().numpy(), Lt.double().cpu().numpy()
     rows = W.sample_rows(w, n_rows)
-    if w.dropout_p is None:
+    if w.dropout_p is None and w.window is None:
         Oref, Lref = run_oracle(q, k, v, mask, causal=w.causal, scale=w.scale, rows=rows)
     else:
         Oref, Lref = attention_fwd(q.double().numpy(), k.double().numpy(), v.double().numpy(), scale=w.scale,
-                                   causal=w.causal, rows=rows, dropout_p=w.dropout_p, seed=w.seed)
+                                   causal=w.causal, rows=rows, dropout_p=w.dropout_p, seed=w.seed, window=w.window)
     D = w.D
     assert_parity(O.reshape(-1, D)[rows], L.reshape(-1)[rows], Oref, Lref, w.dtype, w.name + " sampled")
     # properties of every row: finite; O inside the per-(b, head) range of V;
-    # s_i0 <= L_i <= scale |q_i| max_j |k_j| + ln kL (key 0 is allowed in every row)
+    # s_ij <= L_i <= scale |q_i| max_j |k_j| + ln kL for a key j allowed in
+    # every row: key 0, or the diagonal key under a window
     assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
     grp = w.Hq // w.Hkv
     vmin = v.double().amin(dim=2).repeat_interleave(grp, dim=1).numpy()[:, :, None, :]
@@ -81,7 +83,10 @@ def test_config_full_size_sampled(w, n_rows):
         vabs = np.maximum(np.abs(vmin), np.abs(vmax)) / (1 - w.dropout_p)
         assert np.all(np.abs(O) <= vabs + slack), "O beyond max|V| / (1 - p)"
     qd, kd = q.double(), k.double().repeat_interleave(grp, dim=1)
-    s0 = (qd * kd[:, :, :1, :]).sum(-1).numpy() * w.scale
+    if w.window is None:
+        s0 = (qd * kd[:, :, :1, :]).sum(-1).numpy() * w.scale
+    else:
+        s0 = (qd * kd[:, :, :w.qL, :]).sum(-1).numpy() * w.scale
     ub = w.scale * qd.norm(dim=-1).numpy() * kd.norm(dim=-1).amax(dim=2, keepdim=True).numpy() + math.log(w.kL)
     assert np.all(L >= s0 - TOL_L), "L below the score of key 0"
     assert np.all(L <= ub + TOL_L), "L above its Cauchy-Schwarz bound"
@@ -515,3 +520,74 @@ def test_split_over_more_ranges_than_lanes():
     O, L, _ = run_gpu(q, k, v, scale=1 / math.sqrt(128))
     Oref, Lref = run_oracle(q, k, v, scale=1 / math.sqrt(128))
     assert_parity(O, L, Oref, Lref, "bf16", "split into 128 ranges")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,qL,kL,D,window,kind", [
+    (1, 4, 2, 1000, 1000, 128, 256, "none"),    # ragged, several tiles inside the window
+    (1, 4, 4, 777, 900, 64, 1, "none"),         # the diagonal only
+    (2, 4, 2, 520, 520, 64, 100, "none"),       # window edge inside tiles and waves
+    (1, 2, 1, 300, 300, 256, 64, "none"),       # D = 256 (work-group kernel, never the key split)
+    (1, 4, 2, 300, 333, 16, 33, "none"),
+    (1, 4, 2, 600, 600, 96, 129, "none"),
+    (1, 8, 2, 24, 4000, 128, 7, "none"),        # 32-row tiles packing GQA heads
+    (1, 4, 2, 48, 48, 128, 10, "none"),         # 2-wave short-query shape
+    (1, 2, 2, 100, 100, 128, 5, "none"),        # short keys (not the streaming kernel)
+    (1, 4, 2, 1000, 300, 64, 40, "none"),       # rows past kL + window see no key
+    (1, 4, 2, 400, 500, 64, 70, "additive"),
+    (1, 2, 1, 333, 333, 128, 200, "bool"),
+    (1, 2, 2, 257, 257, 80, 64, "bool"),
+], ids=lambda x: str(x))
+def test_sliding_window_matches_the_oracle(B, Hq, Hkv, qL, kL, D, window, kind):
+    """Causal sliding window (row i sees keys i - window + 1 .. i), element by
+    element against the oracle; rows with no key give O = 0, L = 0 on both sides."""
+    print(f"[case] window={window} B={B} Hq={Hq} Hkv={Hkv} qL={qL} kL={kL} D={D} mask={kind}", flush=True)
+    q, k, v = _rand((B, Hq, qL, D), BF16, 81), _rand((B, Hkv, kL, D), BF16, 82), _rand((B, Hkv, kL, D), BF16, 83)
+    mask = None
+    if kind != "none":
+        rng = np.random.default_rng(84)
+        masked = W.draw_masked(rng, (B, Hq, qL, kL), 0.3)
+        if kind == "bool":
+            mask = torch.from_numpy((~masked).astype(np.uint8))
+        else:
+            m = rng.standard_normal(masked.shape).astype(np.float32)
+            m[masked] = -np.inf
+            mask = torch.from_numpy(m).to(BF16)
+    scale = 1 / math.sqrt(D)
+    dev = torch.device("cuda:0")
+    Od, Ld = fa.fwd(q.to(dev), k.to(dev), v.to(dev), mask=None if mask is None else mask.to(dev), causal=True,
+                    scale=scale, window=window)
+    torch.cuda.synchronize()
+    Od, Ld = Od.double().cpu().numpy(), Ld.double().cpu().numpy()
+    m_np = None if mask is None else (mask.numpy() if kind == "bool" else mask.double().numpy())
+    Oref, Lref = attention_fwd(q.double().numpy(), k.double().numpy(), v.double().numpy(), scale=scale, causal=True,
+                               mask=m_np, mask_kind=kind, window=window)
+    assert_parity(Od, Ld, Oref, Lref, "bf16", f"window={window} qL={qL} kL={kL} D={D} {kind}")
+    empty = np.all(Oref == 0, axis=-1) & (Lref == 0)
+    assert np.all(Od[empty] == 0) and np.all(Ld[empty] == 0)
+
+
+@pytest.mark.parametrize("qL,D", [(2048, 128), (300, 64)])
+def test_a_window_past_every_row_is_plain_causal(qL, D):
+    """window >= qL + 32 takes no tile off the range and masks nothing more:
+    the result is the plain causal one, bit for bit.  32 heads keep the grid
+    large enough that the plain call does not split its key range over
+    work-groups (a windowed call never does)."""
+    dev = torch.device("cuda:0")
+    q = _rand((1, 32, qL, D), BF16, 85).to(dev)
+    k, v = (_rand((1, 8, qL, D), BF16, s).to(dev) for s in (86, 87))
+    O0, L0 = fa.fwd(q, k, v, causal=True)
+    O1, L1 = fa.fwd(q, k, v, causal=True, window=qL + 64)
+    torch.cuda.synchronize()
+    assert torch.equal(O0, O1) and torch.equal(L0, L1)
+
+
+def test_window_rejects_bad_arguments():
+    dev = torch.device("cuda:0")
+    q = torch.zeros((1, 1, 8, 64), dtype=BF16, device=dev)
+    with pytest.raises(fa.FaError, match="window"):
+        fa.fwd(q, q, q, causal=True, window=0)
+    with pytest.raises(fa.FaError, match="causal"):
+        fa.fwd(q, q, q, causal=False, window=4)
+    q32 = q.float()
+    with pytest.raises(fa.FaError, match="no kernel"):
+        fa.fwd(q32, q32, q32, causal=True, window=4)

@@ -40,10 +40,16 @@ class Workload:
     token_major_out: bool = False
     seed: int = 0
     dropout_p: float | None = None  # dropout rate on the attention weights (seed = the workload seed)
+    window: int | None = None       # causal sliding window: row i sees keys i - window + 1 .. i
     note: str = ""
 
     def flops(self) -> float:
-        """Algorithmic FLOP: 4*B*Hq*qL*kL*D, halved when causal."""
+        """Algorithmic FLOP: 4*B*Hq*qL*kL*D, halved when causal; with a window,
+        4*B*Hq*D times the exact count of allowed (row, key) pairs."""
+        if self.window is not None:
+            i = np.arange(self.qL, dtype=np.int64)
+            pairs = np.minimum(np.minimum(i + 1, self.window), np.maximum(0, self.kL - np.maximum(0, i - self.window + 1)))
+            return 4.0 * self.B * self.Hq * self.D * float(pairs.sum())
         f = 4.0 * self.B * self.Hq * self.qL * self.kL * self.D
         return f / 2 if self.causal else f
 
@@ -98,6 +104,13 @@ SPLIT_KV = [
 DROPOUT = [
     Workload("causal_bf16_d128_8k_dropout", "bf16", 1, 32, 8, 8192, 8192, 128, 1 / math.sqrt(128), causal=True,
              seed=70, dropout_p=0.1, note="long-context causal bf16 with dropout 0.1 on the attention weights"),
+]
+
+# The headline shape under a causal sliding window of 4096 keys (the reading
+# taken of the pages' `window` field).
+WINDOW = [
+    Workload("causal_bf16_d128_8k_window4k", "bf16", 1, 32, 8, 8192, 8192, 128, 1 / math.sqrt(128), causal=True,
+             seed=80, window=4096, note="long-context causal bf16 under a 4096-key sliding window"),
 ]
 
 # Ragged shapes that are not tile multiples (the configs above all are).
