@@ -1641,7 +1641,12 @@ const Variant* variants_bf16(int* n)
 const Variant* variants_bf16_dropout(int* n)
 {
     static const Variant table[] = {
+    FA_BF16_DROP_FOR_D(16, FA_BF16_D16_CFG, FA_BF16_D16_MASKED_CFG),
+    FA_BF16_DROP_FOR_D(32, FA_BF16_D32_CFG, FA_BF16_D32_MASKED_CFG),
+    FA_BF16_DROP_FOR_D(48, FA_BF16_D48_CFG, FA_BF16_D48_MASKED_CFG),
     FA_BF16_DROP_FOR_D(64, FA_BF16_D64_CFG, FA_BF16_D64_MASKED_CFG),
+    FA_BF16_DROP_FOR_D(80, FA_BF16_D80_CFG, FA_BF16_D80_MASKED_CFG),
+    FA_BF16_DROP_FOR_D(96, FA_BF16_D96_CFG, FA_BF16_D96_MASKED_CFG),
     FA_BF16_DROP_FOR_D(128, FA_BF16_D128_CFG, FA_BF16_D128_MASKED_CFG),
 };
     *n = (int)(sizeof(table) / sizeof(table[0]));

@@ -455,7 +455,7 @@ def test_short_query_ranges_pack_gqa_heads(Hq, Hkv, qL, kL, D, kind, causal):
         assert np.all(O[1, Hq - 1, qL - 1] == 0) and L[1, Hq - 1, qL - 1] == 0
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [16, 32, 48, 64, 80, 96, 128])
 @pytest.mark.parametrize("p", [0.0, 0.25, 1.0])
 @pytest.mark.parametrize("B,Hq,Hkv,qL,kL,causal,kind", [
     (1, 2, 1, 130, 256, False, "none"),
@@ -506,9 +506,9 @@ def test_dropout_rejects_bad_rates_and_unbuilt_shapes():
     for bad in (-0.1, 1.5, float("nan")):
         with pytest.raises(fa.FaError):
             fa.fwd(q, q, q, dropout_p=bad)
-    q32 = torch.zeros((1, 1, 8, 32), dtype=BF16, device=dev)
-    with pytest.raises(fa.FaError):
-        fa.fwd(q32, q32, q32, dropout_p=0.1)
+    q256 = torch.zeros((1, 1, 8, 256), dtype=BF16, device=dev)  # no dropout kernel at D = 256
+    with pytest.raises(fa.FaError, match="no kernel"):
+        fa.fwd(q256, q256, q256, dropout_p=0.1)
 
 
 def test_split_over_more_ranges_than_lanes():
