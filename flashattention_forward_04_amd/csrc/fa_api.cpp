@@ -177,8 +177,6 @@ fa_status fwd_impl(const void* Q, const void* K, const void* V, const void* mask
         if (s.mask[a] < 0) return fail(E, "fa_fwd: mask strides must be non-negative");
 
     const fa::Variant* var = find_variant(dtype, D, mask_kind, causal, drop != nullptr);
-    if (window > 0 && dtype != FA_DTYPE_BF16)
-        return fail(FA_ERR_UNSUPPORTED, "fa_fwd_window: no kernel built for a sliding window in dtype %d", (int)dtype);
     if (!var)
         return fail(FA_ERR_UNSUPPORTED, "fa_fwd: no kernel built for dtype %d, D %d, mask %d, causal %d",
                     (int)dtype, D, (int)mask_kind, causal);

@@ -41,8 +41,8 @@ struct FwdParams {
     // Work-group kernel: rows [32 t, 32 t + 32) of NW query heads of one GQA
     // group per work-group, one head per wave (short query ranges).
     int head_pack;
-    // Causal sliding window (work-group kernel): window >= 1 restricts row i
-    // to keys i - window + 1 .. i; 0 is no window.
+    // Causal sliding window (the work-group kernels, bf16 and fp32):
+    // window >= 1 restricts row i to keys i - window + 1 .. i; 0 is no window.
     int window;
     // Dropout (the work-group kernel's dropout variants): a P V term is kept
     // when the Philox-4x32-10 word drawn for its score position, as

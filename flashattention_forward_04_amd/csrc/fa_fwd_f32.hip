@@ -96,6 +96,10 @@ fwd_f32_kernel(const FwdParams p)
 
     const float c2 = p.scale_log2;
     const int kv_end = CAUSAL ? min(p.kL, min(p.qL, q0 + BM)) : p.kL;
+    // causal sliding window: rows see keys from i - window + 1 on, so the
+    // work-group starts at the tile of its first row's first key
+    const bool win = CAUSAL && p.window > 0;
+    const int t_first = win ? max(0, q0 - p.window + 1) / BN : 0;
 
     const uint8_t* mrow = nullptr;
     if (MASK != MASK_NONE) {
@@ -127,7 +131,9 @@ fwd_f32_kernel(const FwdParams p)
             }
         }
 
-        const bool fast = (MASK == MASK_NONE) && (j0 + BN <= p.kL) && (!CAUSAL || j0 + BN - 1 <= wq0);
+        // (a tile reaching below the window of the wave's last row is masked too)
+        const bool w_edge = win && j0 < wq0 + 32 - p.window;
+        const bool fast = (MASK == MASK_NONE) && (j0 + BN <= p.kL) && (!CAUSAL || j0 + BN - 1 <= wq0) && !w_edge;
         float cs = c2;
         if (!fast) {
             cs = 1.f;
@@ -163,6 +169,7 @@ fwd_f32_kernel(const FwdParams p)
                         const int j = jb + e;
                         bool ok = (j < p.kL) && mb[e];
                         if (CAUSAL) ok = ok && (j <= qrow);
+                        if (CAUSAL) ok = ok && (!w_edge || j > qrow - p.window);
                         float t = s[c][4 * rq + e] * c2;
                         if (MASK == MASK_ADD) t = __builtin_fmaf(mv[e], kLog2e, t);
                         s[c][4 * rq + e] = ok ? t : -INFINITY;
@@ -273,10 +280,12 @@ fwd_f32_kernel(const FwdParams p)
         }
     };
 
-    // tile 0, then the loop: tile t+1 is loaded (K straight into LDS, V into
-    // registers) while tile t is computed; V goes to LDS after tile t
-    issue_k(0, Ks0);
-    load_v(0);
+    // the first tile, then the loop: tile t+1 is loaded (K straight into
+    // LDS, V into registers) while tile t is computed; V goes to LDS after
+    // tile t.  (Rows past kL are clamped to kL - 1, so a first tile past the
+    // key range loads in bounds and the loop does not run.)
+    issue_k(t_first, Ks0);
+    load_v(t_first);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     store_v(Vt0);
     __syncthreads();
@@ -294,7 +303,7 @@ fwd_f32_kernel(const FwdParams p)
         if (more) store_v(vn);
         __syncthreads();
     };
-    for (int t = 0; t < n_tiles; t += 2) {
+    for (int t = t_first; t < n_tiles; t += 2) {
         step(t, Ks0, Vt0, Ks1, Vt1);
         if (t + 1 < n_tiles) step(t + 1, Ks1, Vt1, Ks0, Vt0);
     }

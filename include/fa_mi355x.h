@@ -152,7 +152,7 @@ fa_status fa_fwd_dropout(const void* Q, const void* K, const void* V, const void
  * generally, >= qL) is plain causal attention.  A row left with no key gets
  * O = 0 and L = 0, as in fa_fwd.
  * window must be >= 1 and causal must be 1 (else FA_ERR_INVALID_ARGUMENT).
- * Built for bf16 at every D and mask kind; fp32 returns FA_ERR_UNSUPPORTED.
+ * Built for bf16 and fp32 at every D and mask kind.
  * A windowed launch never splits its key range over work-groups, so it
  * allocates nothing.  Everything else as fa_fwd_strided.
  */

@@ -184,11 +184,6 @@ def test_window_needs_causal(lib):
     assert "needs causal" in fa.fa_last_error()
 
 
-def test_window_reports_fp32_as_unbuilt(lib):
-    assert _window_call(16, dtype=fa.FA_DTYPE_F32) == fa.FA_ERR_UNSUPPORTED
-    assert "sliding window" in fa.fa_last_error()
-
-
 def test_window_checks_the_plain_arguments_too(lib):
     assert _window_call(16, H_q=3) == fa.FA_ERR_INVALID_ARGUMENT
     assert "divisible" in fa.fa_last_error()

@@ -537,11 +537,12 @@ def test_split_over_more_ranges_than_lanes():
     (1, 2, 1, 333, 333, 128, 200, "bool"),
     (1, 2, 2, 257, 257, 80, 64, "bool"),
 ], ids=lambda x: str(x))
-def test_sliding_window_matches_the_oracle(B, Hq, Hkv, qL, kL, D, window, kind):
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
+def test_sliding_window_matches_the_oracle(B, Hq, Hkv, qL, kL, D, window, kind, dtype):
     """Causal sliding window (row i sees keys i - window + 1 .. i), element by
     element against the oracle; rows with no key give O = 0, L = 0 on both sides."""
-    print(f"[case] window={window} B={B} Hq={Hq} Hkv={Hkv} qL={qL} kL={kL} D={D} mask={kind}", flush=True)
-    q, k, v = _rand((B, Hq, qL, D), BF16, 81), _rand((B, Hkv, kL, D), BF16, 82), _rand((B, Hkv, kL, D), BF16, 83)
+    print(f"[case] window={window} B={B} Hq={Hq} Hkv={Hkv} qL={qL} kL={kL} D={D} mask={kind} {dtype}", flush=True)
+    q, k, v = _rand((B, Hq, qL, D), dtype, 81), _rand((B, Hkv, kL, D), dtype, 82), _rand((B, Hkv, kL, D), dtype, 83)
     mask = None
     if kind != "none":
         rng = np.random.default_rng(84)
@@ -551,7 +552,7 @@ def test_sliding_window_matches_the_oracle(B, Hq, Hkv, qL, kL, D, window, kind):
         else:
             m = rng.standard_normal(masked.shape).astype(np.float32)
             m[masked] = -np.inf
-            mask = torch.from_numpy(m).to(BF16)
+            mask = torch.from_numpy(m).to(dtype)
     scale = 1 / math.sqrt(D)
     dev = torch.device("cuda:0")
     Od, Ld = fa.fwd(q.to(dev), k.to(dev), v.to(dev), mask=None if mask is None else mask.to(dev), causal=True,
@@ -561,7 +562,8 @@ def test_sliding_window_matches_the_oracle(B, Hq, Hkv, qL, kL, D, window, kind):
     m_np = None if mask is None else (mask.numpy() if kind == "bool" else mask.double().numpy())
     Oref, Lref = attention_fwd(q.double().numpy(), k.double().numpy(), v.double().numpy(), scale=scale, causal=True,
                                mask=m_np, mask_kind=kind, window=window)
-    assert_parity(Od, Ld, Oref, Lref, "bf16", f"window={window} qL={qL} kL={kL} D={D} {kind}")
+    assert_parity(Od, Ld, Oref, Lref, "bf16" if dtype == BF16 else "f32",
+                  f"window={window} qL={qL} kL={kL} D={D} {kind}")
     empty = np.all(Oref == 0, axis=-1) & (Lref == 0)
     assert np.all(Od[empty] == 0) and np.all(Ld[empty] == 0)
 
@@ -588,6 +590,3 @@ def test_window_rejects_bad_arguments():
         fa.fwd(q, q, q, causal=True, window=0)
     with pytest.raises(fa.FaError, match="causal"):
         fa.fwd(q, q, q, causal=False, window=4)
-    q32 = q.float()
-    with pytest.raises(fa.FaError, match="no kernel"):
-        fa.fwd(q32, q32, q32, causal=True, window=4)
