@@ -39,7 +39,7 @@ struct DropArgs {
 const fa::Variant* find_variant(int dtype, int D, int mask, int causal, bool dropout = false)
 {
     int n = 0;
-    const fa::Variant* tab = dropout ? (dtype == FA_DTYPE_BF16 ? fa::variants_bf16_dropout(&n) : nullptr)
+    const fa::Variant* tab = dropout ? (dtype == FA_DTYPE_BF16 ? fa::variants_bf16_dropout(&n) : fa::variants_f32_dropout(&n))
                              : dtype == FA_DTYPE_BF16 ? fa::variants_bf16(&n) : fa::variants_f32(&n);
     for (int i = 0; i < n; ++i)
         if (tab[i].D == D && tab[i].mask == mask && tab[i].causal == (causal ? 1 : 0)) return &tab[i];

@@ -112,6 +112,69 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_base) {
         : "memory");
 }
 
+// Philox-4x32 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel
+// random numbers: as easy as 1, 2, 3", SC 2011) on the counter (c0, c1, 0, 0)
+// under the key (k0, k1): each round multiplies words 0 and 2 by the round
+// constants, spreads the 64-bit products as (hi(c2 M1) ^ c1 ^ k0,
+// lo(c2 M1), hi(c0 M0) ^ c3 ^ k1, lo(c0 M0)) and advances the key by the
+// Weyl increments.
+struct Words4 {
+    uint32_t w0, w1, w2, w3;
+};
+__device__ __forceinline__ Words4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1)
+{
+    uint32_t c2 = 0u, c3 = 0u;
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        // one 32 x 32 -> 64-bit product each (a single multiply-add
+        // instruction rather than separate low and high multiplies)
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return Words4{c0, c1, c2, c3};
+}
+__device__ __forceinline__ uint32_t word_at(const Words4& w, int i)
+{
+    return i == 0 ? w.w0 : i == 1 ? w.w1 : i == 2 ? w.w2 : w.w3;
+}
+
+// Dropout multipliers of the 4 consecutive score positions n0 .. n0 + 3
+// (n = ((b H_q + h) qL + i) kL + j): word n mod 4 of the Philox block at
+// counter offset + floor(n / 4) decides key n; a kept term is scaled by
+// drop_scale, a dropped one by 0.
+__device__ __forceinline__ void dropout_quad(const FwdParams& p, int64_t n0, float* mult)
+{
+    const uint64_t off = ((uint64_t)p.off_hi << 32) | p.off_lo;
+    const uint64_t ctr = off + ((uint64_t)n0 >> 2);
+    const Words4 wa = philox4x32_10((uint32_t)ctr, (uint32_t)(ctr >> 32), p.seed_lo, p.seed_hi);
+    // u = floor(w / 2^8) / 2^24 >= p  <=>  floor(w / 2^8) >= ceil(p 2^24)
+    // <=>  w >= ceil(p 2^24) 2^8 = drop_thresh (an integer compare)
+    auto keep = [&](uint32_t w) __attribute__((always_inline)) { return (w >= p.drop_thresh) ? p.drop_scale : 0.f; };
+    if ((p.kL & 3) == 0) {
+        // every row starts at a multiple of 4: one block covers the quad
+        mult[0] = keep(wa.w0);
+        mult[1] = keep(wa.w1);
+        mult[2] = keep(wa.w2);
+        mult[3] = keep(wa.w3);
+    } else {
+        const Words4 wb = philox4x32_10((uint32_t)(ctr + 1), (uint32_t)((ctr + 1) >> 32), p.seed_lo, p.seed_hi);
+        const int sh = (int)(n0 & 3);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = sh + e;
+            mult[e] = keep(i < 4 ? word_at(wa, i) : word_at(wb, i - 4));
+        }
+    }
+}
+
 // One compiled variant: its launch function and shape facts the host needs.
 typedef hipError_t (*LaunchFn)(const FwdParams&, hipStream_t);
 
@@ -129,5 +192,6 @@ struct Variant {
 const Variant* variants_bf16(int* n);
 const Variant* variants_f32(int* n);
 const Variant* variants_bf16_dropout(int* n);
+const Variant* variants_f32_dropout(int* n);
 
 }  // namespace fa

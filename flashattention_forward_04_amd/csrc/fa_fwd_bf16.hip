@@ -148,40 +148,6 @@ __device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
 //
 // K/V tiles are loaded straight from global memory into LDS (no registers),
 // round a ring of NB buffers, with one barrier per tile.
-// Philox-4x32 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel
-// random numbers: as easy as 1, 2, 3", SC 2011) on the counter (c0, c1, 0, 0)
-// under the key (k0, k1): each round multiplies words 0 and 2 by the round
-// constants, spreads the 64-bit products as (hi(c2 M1) ^ c1 ^ k0,
-// lo(c2 M1), hi(c0 M0) ^ c3 ^ k1, lo(c0 M0)) and advances the key by the
-// Weyl increments.
-struct Words4 {
-    uint32_t w0, w1, w2, w3;
-};
-__device__ __forceinline__ Words4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1)
-{
-    uint32_t c2 = 0u, c3 = 0u;
-#pragma unroll
-    for (int round = 0; round < 10; ++round) {
-        // one 32 x 32 -> 64-bit product each (a single multiply-add
-        // instruction rather than separate low and high multiplies)
-        const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
-        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
-        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
-        const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
-        c0 = n0;
-        c1 = lo1;
-        c2 = n2;
-        c3 = lo0;
-        k0 += 0x9E3779B9u;
-        k1 += 0xBB67AE85u;
-    }
-    return Words4{c0, c1, c2, c3};
-}
-__device__ __forceinline__ uint32_t word_at(const Words4& w, int i)
-{
-    return i == 0 ? w.w0 : i == 1 ? w.w1 : i == 2 ? w.w2 : w.w3;
-}
-
 template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB, bool DROP = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fwd_bf16_kernel(const FwdParams p)
@@ -319,31 +285,7 @@ fwd_bf16_kernel(const FwdParams p)
     // dropout: the score position of this lane's row at key 0, and the
     // dropout multipliers of the 4 consecutive keys from position n0
     const int64_t drow = DROP ? (((int64_t)b * p.Hq + h) * p.qL + qrow) * p.kL : 0;
-    auto drop_quad = [&](int64_t n0, float* mult) __attribute__((always_inline)) {
-        const uint64_t off = ((uint64_t)p.off_hi << 32) | p.off_lo;
-        const uint64_t ctr = off + ((uint64_t)n0 >> 2);
-        const Words4 wa = philox4x32_10((uint32_t)ctr, (uint32_t)(ctr >> 32), p.seed_lo, p.seed_hi);
-        // u = floor(w / 2^8) / 2^24 >= p  <=>  floor(w / 2^8) >= ceil(p 2^24)
-        // <=>  w >= ceil(p 2^24) 2^8 = drop_thresh (an integer compare)
-        auto keep = [&](uint32_t w) __attribute__((always_inline)) {
-            return (w >= p.drop_thresh) ? p.drop_scale : 0.f;
-        };
-        if ((p.kL & 3) == 0) {
-            // every row starts at a multiple of 4: one block covers the quad
-            mult[0] = keep(wa.w0);
-            mult[1] = keep(wa.w1);
-            mult[2] = keep(wa.w2);
-            mult[3] = keep(wa.w3);
-        } else {
-            const Words4 wb = philox4x32_10((uint32_t)(ctr + 1), (uint32_t)((ctr + 1) >> 32), p.seed_lo, p.seed_hi);
-            const int sh = (int)(n0 & 3);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = sh + e;
-                mult[e] = keep(i < 4 ? word_at(wa, i) : word_at(wb, i - 4));
-            }
-        }
-    };
+    auto drop_quad = [&](int64_t n0, float* mult) __attribute__((always_inline)) { dropout_quad(p, n0, mult); };
 
     // mask row of this lane (clamped so ragged rows read in bounds)
     const uint8_t* mrow = nullptr;

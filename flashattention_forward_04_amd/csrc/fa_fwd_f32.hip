@@ -37,7 +37,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
-template <int D, int MASK, bool CAUSAL, int NW, int BN>
+template <int D, int MASK, bool CAUSAL, int NW, int BN, bool DROP = false>
 __global__ void __launch_bounds__(NW * 64)
 fwd_f32_kernel(const FwdParams p)
 {
@@ -93,6 +93,9 @@ fwd_f32_kernel(const FwdParams p)
 #pragma unroll
         for (int t = 0; t < DT; ++t) qf[t] = in ? src[2 * t + g] * sgn : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+
+    // dropout: the score position of this lane's row at key 0
+    const int64_t drow = DROP ? (((int64_t)b * p.Hq + h) * p.qL + qrow) * p.kL : 0;
 
     const float c2 = p.scale_log2;
     const int kv_end = CAUSAL ? min(p.kL, min(p.qL, q0 + BM)) : p.kL;
@@ -201,6 +204,19 @@ fwd_f32_kernel(const FwdParams p)
         m_run = m_new;
 #pragma unroll
         for (int d = 0; d < ND; ++d) o[d] *= corr;
+        if constexpr (DROP) {
+            // the row sum above takes P before dropout (l and L are those
+            // without it); only the P V product sees the multipliers
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    float mlt[4];
+                    dropout_quad(p, drow + j0 + 32 * c + 8 * rq + 4 * g, mlt);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s[c][4 * rq + e] *= mlt[e];
+                }
+        }
 
         // ---- O^T += V^T P^T: step r of key block c is key 32c + 8(r/4) + 4g + r%4 ----
 #pragma unroll
@@ -326,13 +342,13 @@ fwd_f32_kernel(const FwdParams p)
     }
 }
 
-template <int D, int MASK, bool CAUSAL, int NW, int BN>
+template <int D, int MASK, bool CAUSAL, int NW, int BN, bool DROP = false>
 hipError_t launch_f32(const FwdParams& p, hipStream_t st)
 {
     FwdParams q = p;
     const int64_t wgs = (int64_t)p.n_qtiles * p.Hq * p.B;
     q.pair_tiles = CAUSAL && grid_fits_at_once(wgs, 1);
-    hipLaunchKernelGGL((fwd_f32_kernel<D, MASK, CAUSAL, NW, BN>), dim3((unsigned)wgs), dim3(NW * 64), 0, st, q);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, MASK, CAUSAL, NW, BN, DROP>), dim3((unsigned)wgs), dim3(NW * 64), 0, st, q);
     return hipGetLastError();
 }
 
@@ -391,6 +407,34 @@ const Variant* variants_f32(int* n)
     FA_F32_FOR_D_CFG(96, FA_F32_D96_CFG),
     FA_F32_FOR_D_CFG(128, FA_F32_D128_CFG),
     FA_F32_FOR_D_CFG(256, FA_F32_D256_CFG),
+};
+    *n = (int)(sizeof(table) / sizeof(table[0]));
+    return table;
+}
+
+// Dropout variants: the same kernel at the same launch shapes, with the
+// multipliers applied to the fp32 P before P V.
+#define FA_F32_DROP_VARIANT(D, MASK, CAUSAL, NW, BN, NAME) \
+    {NAME, 0, D, MASK, CAUSAL, NW * 32, &launch_f32<D, MASK, CAUSAL, NW, BN, true>}
+#define FA_F32_DROP_FOR_D(D, NW, BN)                                                           \
+    FA_F32_DROP_VARIANT(D, MASK_NONE, false, NW, BN, "fwd_f32_d" #D "_nomask_dropout"),        \
+    FA_F32_DROP_VARIANT(D, MASK_NONE, true, NW, BN, "fwd_f32_d" #D "_nomask_causal_dropout"),  \
+    FA_F32_DROP_VARIANT(D, MASK_ADD, false, NW, BN, "fwd_f32_d" #D "_additive_dropout"),       \
+    FA_F32_DROP_VARIANT(D, MASK_ADD, true, NW, BN, "fwd_f32_d" #D "_additive_causal_dropout"), \
+    FA_F32_DROP_VARIANT(D, MASK_BOOL, false, NW, BN, "fwd_f32_d" #D "_bool_dropout"),          \
+    FA_F32_DROP_VARIANT(D, MASK_BOOL, true, NW, BN, "fwd_f32_d" #D "_bool_causal_dropout")
+#define FA_F32_DROP_FOR_D_CFG(D, ...) FA_F32_DROP_FOR_D(D, __VA_ARGS__)
+
+const Variant* variants_f32_dropout(int* n)
+{
+    static const Variant table[] = {
+    FA_F32_DROP_FOR_D_CFG(16, FA_F32_D16_CFG),
+    FA_F32_DROP_FOR_D_CFG(32, FA_F32_D32_CFG),
+    FA_F32_DROP_FOR_D_CFG(48, FA_F32_D48_CFG),
+    FA_F32_DROP_FOR_D_CFG(64, FA_F32_D64_CFG),
+    FA_F32_DROP_FOR_D_CFG(80, FA_F32_D80_CFG),
+    FA_F32_DROP_FOR_D_CFG(96, FA_F32_D96_CFG),
+    FA_F32_DROP_FOR_D_CFG(128, FA_F32_D128_CFG),
 };
     *n = (int)(sizeof(table) / sizeof(table[0]));
     return table;

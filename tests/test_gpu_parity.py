@@ -455,6 +455,7 @@ def test_short_query_ranges_pack_gqa_heads(Hq, Hkv, qL, kL, D, kind, causal):
         assert np.all(O[1, Hq - 1, qL - 1] == 0) and L[1, Hq - 1, qL - 1] == 0
 
 
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("D", [16, 32, 48, 64, 80, 96, 128])
 @pytest.mark.parametrize("p", [0.0, 0.25, 1.0])
 @pytest.mark.parametrize("B,Hq,Hkv,qL,kL,causal,kind", [
@@ -463,16 +464,16 @@ def test_short_query_ranges_pack_gqa_heads(Hq, Hkv, qL, kL, D, kind, causal):
     (1, 2, 2, 64, 150, False, "bool"),
     (1, 4, 1, 16, 4096, False, "additive"),
 ], ids=lambda x: str(x))
-def test_dropout_matches_the_oracle(D, p, B, Hq, Hkv, qL, kL, causal, kind):
+def test_dropout_matches_the_oracle(D, p, B, Hq, Hkv, qL, kL, causal, kind, dtype):
     """Dropout on the attention weights: the keep mask is drawn from the same
     Philox-4x32-10 positions on both sides, so O matches element by element;
     L is the one without dropout.  kL = 203 and 150 put rows at offsets that
     are not multiples of 4 (two generator blocks per 4 keys); 16 rows over
     4096 keys split the key range over work-groups."""
     seed, offset = 0x9E3779B97F4A7C15, (1 << 33) + 5
-    print(f"[case] dropout p={p} B={B} Hq={Hq} Hkv={Hkv} qL={qL} kL={kL} D={D} mask={kind} causal={causal}",
+    print(f"[case] dropout p={p} B={B} Hq={Hq} Hkv={Hkv} qL={qL} kL={kL} D={D} mask={kind} causal={causal} {dtype}",
           flush=True)
-    q, k, v = _rand((B, Hq, qL, D), BF16, 61), _rand((B, Hkv, kL, D), BF16, 62), _rand((B, Hkv, kL, D), BF16, 63)
+    q, k, v = _rand((B, Hq, qL, D), dtype, 61), _rand((B, Hkv, kL, D), dtype, 62), _rand((B, Hkv, kL, D), dtype, 63)
     mask = None
     if kind != "none":
         rng = np.random.default_rng(64)
@@ -482,7 +483,7 @@ def test_dropout_matches_the_oracle(D, p, B, Hq, Hkv, qL, kL, causal, kind):
         else:
             m = rng.standard_normal(masked.shape).astype(np.float32)
             m[masked] = -np.inf
-            mask = torch.from_numpy(m).to(BF16)
+            mask = torch.from_numpy(m).to(dtype)
     scale = 1 / math.sqrt(D)
     dev = torch.device("cuda:0")
     Od, Ld = fa.fwd(q.to(dev), k.to(dev), v.to(dev), mask=None if mask is None else mask.to(dev), causal=causal,
@@ -494,7 +495,8 @@ def test_dropout_matches_the_oracle(D, p, B, Hq, Hkv, qL, kL, causal, kind):
     Oref, Lref = attention_fwd(q.double().numpy(), k.double().numpy(), v.double().numpy(), scale=scale, causal=causal,
                                mask=m_np, mask_kind=kindname, dropout_p=p, seed=seed, offset=offset)
     _, Lplain = run_oracle(q, k, v, mask, causal=causal, scale=scale)
-    assert_parity(Od, Ld, Oref, Lref, "bf16", f"dropout p={p} qL={qL} kL={kL} D={D} {kind} causal={causal}")
+    assert_parity(Od, Ld, Oref, Lref, "bf16" if dtype == BF16 else "f32",
+                  f"dropout p={p} qL={qL} kL={kL} D={D} {kind} causal={causal}")
     assert np.max(np.abs(Ld - Lplain)) <= TOL_L
     if p == 1.0:
         assert np.all(Od == 0)
