@@ -160,10 +160,10 @@ def fwd(q, k, v, *, mask=None, causal=False, scale=None, out=None, lse=None, str
     [B, H_q, qL] contiguous.  scale defaults to 1/sqrt(D).
     The call is asynchronous on `stream` (default: torch's current stream).
     dropout_p: None, or a rate in [0, 1] for dropout on the attention weights
-    under the 64-bit `seed` and counter `offset` (fa_fwd_dropout; bf16 at
-    every D but 256).
+    under the 64-bit `seed` and counter `offset` (fa_fwd_dropout; bf16 or
+    fp32 at every D but 256).
     window: None, or a causal sliding window of that many keys (row i sees
-    keys i - window + 1 .. i; fa_fwd_window, bf16, causal only).
+    keys i - window + 1 .. i; fa_fwd_window, causal only).
     """
     import torch
 
