@@ -161,7 +161,7 @@ def fwd(q, k, v, *, mask=None, causal=False, scale=None, out=None, lse=None, str
     The call is asynchronous on `stream` (default: torch's current stream).
     dropout_p: None, or a rate in [0, 1] for dropout on the attention weights
     under the 64-bit `seed` and counter `offset` (fa_fwd_dropout; bf16 or
-    fp32 at every D but 256).
+    fp32 at every D).
     window: None, or a causal sliding window of that many keys (row i sees
     keys i - window + 1 .. i; fa_fwd_window, causal only).
     """

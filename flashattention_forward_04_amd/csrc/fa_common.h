@@ -48,7 +48,7 @@ struct FwdParams {
     // when the Philox-4x32-10 word drawn for its score position, as
     // u = (word >> 8) / 2^24, is >= drop_p, and then scaled by drop_scale.
     float drop_p;
-    float drop_scale;           // 1 / (1 - p), 0 when p >= 1
+    float drop_scale;           // 1 / (1 - p), 0 when p >= 1 (applied to O at the end)
     uint32_t drop_thresh;       // ceil(p 2^24) 2^8 (mod 2^32): keep iff the word is >= it
     uint32_t seed_lo, seed_hi;  // the generator's key
     uint32_t off_lo, off_hi;    // 64-bit offset added to every counter
@@ -146,10 +146,11 @@ __device__ __forceinline__ uint32_t word_at(const Words4& w, int i)
     return i == 0 ? w.w0 : i == 1 ? w.w1 : i == 2 ? w.w2 : w.w3;
 }
 
-// Dropout multipliers of the 4 consecutive score positions n0 .. n0 + 3
+// Keep bits of the 4 consecutive score positions n0 .. n0 + 3
 // (n = ((b H_q + h) qL + i) kL + j): word n mod 4 of the Philox block at
-// counter offset + floor(n / 4) decides key n; a kept term is scaled by
-// drop_scale, a dropped one by 0.
+// counter offset + floor(n / 4) decides key n; 1 keeps the term, 0 drops it.
+// The kernels apply the common 1 / (1 - p) to O at the end, so P times a
+// keep bit stays exact in bf16.
 __device__ __forceinline__ void dropout_quad(const FwdParams& p, int64_t n0, float* mult)
 {
     const uint64_t off = ((uint64_t)p.off_hi << 32) | p.off_lo;
@@ -157,7 +158,7 @@ __device__ __forceinline__ void dropout_quad(const FwdParams& p, int64_t n0, flo
     const Words4 wa = philox4x32_10((uint32_t)ctr, (uint32_t)(ctr >> 32), p.seed_lo, p.seed_hi);
     // u = floor(w / 2^8) / 2^24 >= p  <=>  floor(w / 2^8) >= ceil(p 2^24)
     // <=>  w >= ceil(p 2^24) 2^8 = drop_thresh (an integer compare)
-    auto keep = [&](uint32_t w) __attribute__((always_inline)) { return (w >= p.drop_thresh) ? p.drop_scale : 0.f; };
+    auto keep = [&](uint32_t w) __attribute__((always_inline)) { return (w >= p.drop_thresh) ? 1.f : 0.f; };
     if ((p.kL & 3) == 0) {
         // every row starts at a multiple of 4: one block covers the quad
         mult[0] = keep(wa.w0);

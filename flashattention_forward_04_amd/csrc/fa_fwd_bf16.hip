@@ -722,7 +722,8 @@ fwd_bf16_kernel(const FwdParams p)
     if (qrow < p.qL && head_ok && p.n_split > 1) {
         // one key range of a split launch: normalised fp32 O and natural-log
         // L of this range (-inf when it holds no allowed key)
-        const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
+        // dropout's 1 / (1 - p) scales every kept term alike: it is applied here
+        const float inv = (l_run > 0.f) ? (DROP ? p.drop_scale : 1.f) / l_run : 0.f;
         const int64_t rows = (int64_t)p.B * p.Hq * p.qL;
         const int64_t row = ((int64_t)b * p.Hq + h) * p.qL + qrow;
         float* orow = p.o_part + ((int64_t)split * rows + row) * D;
@@ -738,7 +739,8 @@ fwd_bf16_kernel(const FwdParams p)
             p.l_part[(int64_t)split * rows + row] =
                 (l_run > 0.f) ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : -INFINITY;
     } else if (qrow < p.qL && head_ok) {
-        const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
+        // dropout's 1 / (1 - p) scales every kept term alike: it is applied here
+        const float inv = (l_run > 0.f) ? (DROP ? p.drop_scale : 1.f) / l_run : 0.f;
         uint16_t* orow = (uint16_t*)p.o + b * p.o_s[0] + h * p.o_s[1] + (int64_t)qrow * p.o_s[2];
 #pragma unroll
         for (int d = 0; d < ND; ++d)
@@ -1590,6 +1592,7 @@ const Variant* variants_bf16_dropout(int* n)
     FA_BF16_DROP_FOR_D(80, FA_BF16_D80_CFG, FA_BF16_D80_MASKED_CFG),
     FA_BF16_DROP_FOR_D(96, FA_BF16_D96_CFG, FA_BF16_D96_MASKED_CFG),
     FA_BF16_DROP_FOR_D(128, FA_BF16_D128_CFG, FA_BF16_D128_MASKED_CFG),
+    FA_BF16_DROP_FOR_D(256, FA_BF16_D256_CFG, FA_BF16_D256_MASKED_CFG),
 };
     *n = (int)(sizeof(table) / sizeof(table[0]));
     return table;

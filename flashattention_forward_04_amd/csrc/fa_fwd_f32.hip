@@ -325,7 +325,8 @@ fwd_f32_kernel(const FwdParams p)
     }
 
     if (qrow < p.qL) {
-        const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
+        // dropout's 1 / (1 - p) scales every kept term alike: it is applied here
+        const float inv = (l_run > 0.f) ? (DROP ? p.drop_scale : 1.f) / l_run : 0.f;
         float* orow = (float*)p.o + b * p.o_s[0] + h * p.o_s[1] + (int64_t)qrow * p.o_s[2];
 #pragma unroll
         for (int d = 0; d < ND; ++d)
@@ -435,6 +436,7 @@ const Variant* variants_f32_dropout(int* n)
     FA_F32_DROP_FOR_D_CFG(80, FA_F32_D80_CFG),
     FA_F32_DROP_FOR_D_CFG(96, FA_F32_D96_CFG),
     FA_F32_DROP_FOR_D_CFG(128, FA_F32_D128_CFG),
+    FA_F32_DROP_FOR_D_CFG(256, FA_F32_D256_CFG),
 };
     *n = (int)(sizeof(table) / sizeof(table[0]));
     return table;

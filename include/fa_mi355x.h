@@ -132,8 +132,9 @@ fa_status fa_fwd_strided(const void* Q, const void* K, const void* V, const void
  * reproduces the same mask; a caller drawing several masks advances offset
  * by ceil(B * H_q * qL * kL / 4) between calls.
  * p_drop must lie in [0, 1] (else FA_ERR_INVALID_ARGUMENT).  Built for bf16
- * and fp32 at D = 16, 32, 48, 64, 80, 96 and 128, every mask kind, causal
- * or not; D = 256 returns FA_ERR_UNSUPPORTED.  Everything else as fa_fwd_strided.
+ * and fp32 at every D, every mask kind, causal or not (the work-group
+ * kernels at each head dim's launch shape; D = 256 never takes the key-split
+ * kernel here).  Everything else as fa_fwd_strided.
  */
 fa_status fa_fwd_dropout(const void* Q, const void* K, const void* V, const void* mask,
                          void* O, float* L,
