@@ -106,3 +106,13 @@ def test_rejects_windows_outside_the_reading(kw):
     q, k, v = draw(7)
     with pytest.raises(ValueError):
         attention_fwd(q, k, v, scale=0.3, **kw)
+
+
+@pytest.mark.parametrize("qL,kL,W", [(10, 6, 3), (17, 17, 5), (8, 20, 100), (33, 12, 1)])
+def test_workload_flop_count_is_the_allowed_pair_count(qL, kL, W):
+    """The benchmark's FLOP figure for a windowed workload: 4 D per allowed
+    (row, key) pair, counted here one pair at a time."""
+    import workloads as Wl
+    w = Wl.WINDOW[0].with_(B=1, Hq=1, Hkv=1, qL=qL, kL=kL, D=1, window=W)
+    pairs = sum(1 for i in range(qL) for j in range(kL) if j <= i and i - j < W)
+    assert w.flops() == 4.0 * pairs
