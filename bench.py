@@ -79,14 +79,82 @@ def _read_counter_csv(path, counter):
     return out
 
 
+# rocprofv3 passes of one profile (bench.py --profile).  The trace of record
+# uses the protocol the benchmark line is measured with (5 warm-up launches,
+# 20 timed); the steady-state trace lets the clock settle first.  Counters
+# are taken in runs of their own, a few per pass, never beside a trace.
+DRIVER_PROTOCOL = "--steps 20 --warmup 5"
+STEADY_PROTOCOL = "--steps 100 --warmup 100"
+N_XCD = 8       # MI355X: 8 XCDs (GRBM_GUI_ACTIVE is summed over them)
+N_SIMD = 1024   # 256 CUs x 4 SIMDs
+N_CU = 256
+
+
+def counter_set(w):
+    """The per-dispatch counters of the profile: clock, matrix-core busy
+    cycles and operations, vector and transcendental instructions, LDS bank
+    conflicts (one --pmc pass: 7 SQ counters and 1 GRBM)."""
+    mops = "SQ_INSTS_VALU_MFMA_MOPS_BF16" if w.dtype == "bf16" else "SQ_INSTS_VALU_MFMA_MOPS_F32"
+    return ["GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_WAVES", "SQ_INSTS_VALU",
+            "SQ_INSTS_VALU_TRANS_F32", mops, "SQ_LDS_BANK_CONFLICT"]
+
+
+def profile_commands(prof_dir, w):
+    base = f" --workload {w.name}" if w.name != "causal_bf16_d128_8k" else ""
+    counters = " ".join(counter_set(w))
+    return {
+        "copy_mib": 1024,
+        "trace": f"rocprofv3 --kernel-trace --stats --output-format csv -d {prof_dir}/trace -o trace -- "
+                 f"python3 bench.py {DRIVER_PROTOCOL}{base}",
+        "steady": f"rocprofv3 --kernel-trace --stats --output-format csv -d {prof_dir}/steady -o steady -- "
+                  f"python3 bench.py {STEADY_PROTOCOL} --no-cpu-baseline{base}",
+        "counters": f"rocprofv3 --pmc {counters} --output-format csv -d {prof_dir}/counters -o counters -- "
+                    f"python3 bench.py {DRIVER_PROTOCOL} --no-cpu-baseline{base}",
+        "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {prof_dir}/fetch -o fetch -- "
+                 f"python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline{base}",
+        "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {prof_dir}/write -o write -- "
+                 f"python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline{base}",
+        "copyf": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {prof_dir}/copyf -o copyf -- "
+                 "python3 bench.py --copy-calibration-mib 1024",
+        "copyw": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {prof_dir}/copyw -o copyw -- "
+                 "python3 bench.py --copy-calibration-mib 1024",
+    }
+
+
+def run_profile(prof_dir, w):
+    """Run every rocprofv3 pass of the profile as a child process (this
+    process never touches the GPU), each under a time limit of its own, then
+    summarise.  Stops at the first pass that fails."""
+    import shlex
+    import subprocess
+
+    cmds = profile_commands(prof_dir, w)
+    limits = {"trace": 600, "steady": 300, "counters": 120, "fetch": 90, "write": 90, "copyf": 90, "copyw": 90}
+    os.makedirs(prof_dir, exist_ok=True)
+    for name in ("trace", "steady", "counters", "fetch", "write", "copyf", "copyw"):
+        log(f"[profile] {w.name}: {name} pass")
+        with open(os.path.join(prof_dir, f"{name}.log"), "w") as f:
+            try:
+                r = subprocess.run(shlex.split(cmds[name]), cwd=ROOT, stdout=f, stderr=subprocess.STDOUT,
+                                   timeout=limits[name], env={**os.environ, "TMPDIR": "/tmp"})
+            except subprocess.TimeoutExpired:
+                raise SystemExit(f"[profile] {name} pass timed out after {limits[name]} s")
+        if r.returncode != 0:
+            raise SystemExit(f"[profile] {name} pass failed with status {r.returncode} "
+                             f"(see {prof_dir}/{name}.log)")
+    summarize(prof_dir, w, cmds)
+
+
 def summarize(prof_dir, w, commands):
     """Write profiles/<workload>.md (+ .traffic.json) from rocprofv3 outputs.
 
-    prof_dir holds the outputs of: a --kernel-trace --stats run (trace/),
-    FETCH_SIZE and WRITE_SIZE runs of the workload (fetch/, write/), and the
-    same two counters on a device copy of known size (copyf/, copyw/).
-    The counters are KiB per dispatch; each is scaled by (known copy bytes /
-    what the counter reads for that copy).
+    prof_dir holds the outputs of the passes in profile_commands: kernel
+    traces under the benchmark's protocol (trace/) and after a long warm-up
+    (steady/), one counter pass (counters/), FETCH_SIZE and WRITE_SIZE runs of
+    the workload (fetch/, write/), and the same two counters on a device copy
+    of known size (copyf/, copyw/).  FETCH_SIZE and WRITE_SIZE are KiB per
+    dispatch; each is scaled by (known copy bytes / what the counter reads for
+    that copy).
     """
     import csv
     import glob
@@ -97,28 +165,35 @@ def summarize(prof_dir, w, commands):
             raise FileNotFoundError(os.path.join(prof_dir, pattern))
         return hits[0]
 
-    stats = list(csv.DictReader(open(one("trace/*kernel_stats.csv"))))
-    fa_rows = [r for r in stats if "fa::" in r["Name"]]
-    if not fa_rows:
-        raise RuntimeError("no fa:: kernel in the kernel-trace stats")
-    # one call may launch more than one kernel (a split key range: the
-    # partials, then their merge); the dominant one names the profile and the
-    # per-call figures add up every kernel of the call
-    fa_rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    k = fa_rows[0]
-    avg_us = float(k["AverageNs"]) / 1e3
-    trace = list(csv.DictReader(open(one("trace/*kernel_trace.csv"))))
+    def trace_summary(sub, steps):
+        stats = list(csv.DictReader(open(one(f"{sub}/*kernel_stats.csv"))))
+        rows = [r for r in stats if "fa::" in r["Name"]]
+        if not rows:
+            raise RuntimeError(f"no fa:: kernel in the {sub} kernel-trace stats")
+        # one call may launch more than one kernel (a split key range: the
+        # partials, then their merge); the dominant one names the profile and
+        # the per-call figures add up every kernel of the call
+        rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+        trace = list(csv.DictReader(open(one(f"{sub}/*kernel_trace.csv"))))
+        per = []
+        for r in rows:
+            disp = sorted((x for x in trace if x["Kernel_Name"] == r["Name"]), key=lambda x: int(x["Start_Timestamp"]))
+            durs = [(int(x["End_Timestamp"]) - int(x["Start_Timestamp"])) / 1e3 for x in disp]
+            timed = durs[-steps:]  # the timed steps are the last dispatches
+            per.append((r, sum(timed) / len(timed), len(timed), durs))
+        return per
 
-    def timed_avg(name):
-        # the timed steps are the last `steps` dispatches of the kernel (the
-        # earlier ones are bench.py's warm-up calls)
-        disp = sorted((r for r in trace if r["Kernel_Name"] == name), key=lambda r: int(r["Start_Timestamp"]))
-        timed = disp[-commands["steps"]:]
-        return sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in timed) / len(timed) / 1e3, len(timed)
+    def n_steps(cmd):
+        return int(cmd.split("--steps ")[1].split()[0])
 
-    per_kernel = [(r, *timed_avg(r["Name"])) for r in fa_rows]
-    timed_us = sum(t for _, t, _ in per_kernel)
+    per_kernel = trace_summary("trace", n_steps(commands["trace"]))
+    timed_us = sum(t for _, t, _, _ in per_kernel)
     n_timed = per_kernel[0][2]
+    k = per_kernel[0][0]
+    steady_us = None
+    if glob.glob(os.path.join(prof_dir, "steady/*kernel_stats.csv")):
+        steady = trace_summary("steady", n_steps(commands["steady"]))
+        steady_us = sum(t for _, t, _, _ in steady)
     copy_bytes = commands["copy_mib"] << 20
 
     def scale(counter, sub_run, sub_copy):
@@ -135,25 +210,85 @@ def summarize(prof_dir, w, commands):
     fetch, write = f_raw * f_factor, w_raw * w_factor
     flops = w.flops()
     alg = algorithmic_bytes(w)
+    peak = PEAK_TFLOPS[w.dtype]
+
+    # ---- counters, per dispatch of the dominant kernel ----
+    ctr_lines = []
+    ctr_rec = None
+    if glob.glob(os.path.join(prof_dir, "counters/*counter_collection.csv")):
+        rows = list(csv.DictReader(open(one("counters/*counter_collection.csv"))))
+        disp = {}
+        for r in rows:
+            if r["Kernel_Name"] != k["Name"]:
+                continue
+            d = disp.setdefault(int(r["Dispatch_Id"]), {"t0": int(r["Start_Timestamp"]), "t1": int(r["End_Timestamp"])})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        order = sorted(disp.values(), key=lambda d: d["t0"])
+        mops = counter_set(w)[6]
+
+        def derived(d):
+            ns = d["t1"] - d["t0"]
+            cyc = d["GRBM_GUI_ACTIVE"] / N_XCD  # GPU cycles of the dispatch
+            return {"us": ns / 1e3, "ghz": cyc / ns, "cycles": cyc,
+                    "mfma_busy": d["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * cyc),
+                    "cu_busy": 4 * d["SQ_BUSY_CU_CYCLES"] / (N_CU * cyc),
+                    "valu_per_wave": d["SQ_INSTS_VALU"] / max(1.0, d["SQ_WAVES"]),
+                    "trans_per_wave": d["SQ_INSTS_VALU_TRANS_F32"] / max(1.0, d["SQ_WAVES"]),
+                    "mfma_flop": d[mops] * 512,
+                    "lds_conflict": d["SQ_LDS_BANK_CONFLICT"] / (N_CU * cyc)}
+
+        der = [derived(d) for d in order]
+        timed = der[-n_timed:]
+        avg = {key: sum(x[key] for x in timed) / len(timed) for key in timed[0]}
+        ctr_rec = avg
+        ctr_lines = [
+            "## Counters (one rocprofv3 --pmc pass under the benchmark's protocol)",
+            "",
+            "```",
+            commands["counters"],
+            "```",
+            "",
+            f"Clock = GRBM_GUI_ACTIVE / {N_XCD} XCDs / dispatch time; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+            f"({N_SIMD} SIMDs x cycles); CU busy = 4 SQ_BUSY_CU_CYCLES / ({N_CU} CUs x cycles); matrix FLOP = "
+            f"{mops} x 512; LDS conflict = SQ_LDS_BANK_CONFLICT / ({N_CU} CUs x cycles).  Timings under --pmc "
+            "are serialised dispatches, so they differ from the trace above.",
+            "",
+            f"Averages over the {len(timed)} timed dispatches: clock {avg['ghz']:.3f} GHz, "
+            f"{avg['cycles'] / 1e6:.3f} M cycles, MFMA busy {avg['mfma_busy']:.3f}, CU busy {avg['cu_busy']:.3f}, "
+            f"{avg['valu_per_wave']:.0f} VALU and {avg['trans_per_wave']:.0f} transcendental instructions per wave, "
+            f"matrix FLOP {avg['mfma_flop']:.4g} ({avg['mfma_flop'] / flops:.3f}x the algorithmic {flops:.4g}), "
+            f"LDS bank-conflict cycles {100 * avg['lds_conflict']:.2f} % of CU cycles.",
+            "",
+            f"At the measured clock the matrix peak is {peak * avg['ghz'] / 2.4:.1f} TFLOP/s "
+            f"({peak} at 2.4 GHz).",
+            "",
+            "| dispatch | us | GHz | MFMA busy | CU busy | VALU/wave |",
+            "|---|---|---|---|---|---|",
+            *[f"| {i + 1}{' (timed)' if i >= len(der) - n_timed else ''} | {x['us']:.1f} | {x['ghz']:.3f} | "
+              f"{x['mfma_busy']:.3f} | {x['cu_busy']:.3f} | {x['valu_per_wave']:.0f} |" for i, x in enumerate(der[:25])],
+            "",
+        ]
+
     os.makedirs(PROFILES, exist_ok=True)
-    rec = {"workload": w.name, "kernel": k["Name"], "calls": int(k["Calls"]), "avg_us": avg_us,
-           "timed_steps": n_timed, "timed_avg_us": timed_us,
-           "kernels": [{"name": r["Name"], "timed_avg_us": t} for r, t, _ in per_kernel],
+    rec = {"workload": w.name, "kernel": k["Name"], "calls": int(k["Calls"]),
+           "protocol": commands["trace"].split("bench.py ")[1],
+           "timed_steps": n_timed, "timed_avg_us": timed_us, "steady_avg_us": steady_us,
+           "kernels": [{"name": r["Name"], "timed_avg_us": t} for r, t, _, _ in per_kernel],
            "min_us": float(k["MinNs"]) / 1e3, "max_us": float(k["MaxNs"]) / 1e3,
            "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
            "hbm_bytes_per_launch": fetch + write, "algorithmic_bytes": alg,
-           "fetch_scale": f_factor, "write_scale": w_factor,
+           "fetch_scale": f_factor, "write_scale": w_factor, "counters": ctr_rec,
            "source_sha256": kernel_source_hash()}
     with open(os.path.join(PROFILES, f"{w.name}.traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
-    peak = PEAK_TFLOPS[w.dtype]
+    first = per_kernel[0][3]
     lines = [
         f"# {k['Name']} -- {w.name}",
         "",
         f"Workload: {w.note}; B={w.B} H_q={w.Hq} H_kv={w.Hkv} qL={w.qL} kL={w.kL} D={w.D} {w.dtype} "
         f"causal={w.causal} mask={w.mask_kind}.  FLOP per launch {flops:.4g}; algorithmic bytes {alg:.4g}.",
         "",
-        "## Kernel duration (rocprofv3 --kernel-trace --stats)",
+        "## Kernel duration (rocprofv3 --kernel-trace --stats), the benchmark's protocol",
         "",
         "```",
         commands["trace"],
@@ -162,12 +297,29 @@ def summarize(prof_dir, w, commands):
         f"| kernel | calls | avg us (all) | avg us (last {n_timed} = timed steps) | min us | max us |",
         "|---|---|---|---|---|---|",
         *[f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {t:.1f} | "
-          f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |" for r, t, _ in per_kernel],
+          f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |" for r, t, _, _ in per_kernel],
         "",
-        f"Per call (every kernel above, timed steps): {timed_us:.1f} us, "
+        f"**Per call (every kernel above, timed steps): {timed_us:.1f} us, "
         f"{flops / (timed_us * 1e-6) / 1e12:.1f} TFLOP/s, {100 * flops / (timed_us * 1e-6) / 1e12 / peak:.1f} % of "
-        f"{peak} TFLOP/s.",
+        f"{peak} TFLOP/s.**",
         "",
+        "Dominant kernel, every dispatch in order (warm-up, then timed), us: " + " ".join(f"{x:.0f}" for x in first),
+        "",
+    ]
+    if steady_us is not None:
+        lines += [
+            "## Steady state (same trace after a long warm-up)",
+            "",
+            "```",
+            commands["steady"],
+            "```",
+            "",
+            f"Per call: {steady_us:.1f} us, {flops / (steady_us * 1e-6) / 1e12:.1f} TFLOP/s, "
+            f"{100 * flops / (steady_us * 1e-6) / 1e12 / peak:.1f} % of {peak} TFLOP/s.",
+            "",
+        ]
+    lines += ctr_lines
+    lines += [
         "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, summed over the call's kernels)",
         "",
         "```",
@@ -188,7 +340,8 @@ def summarize(prof_dir, w, commands):
         "",
         f"At the timed average: algorithmic {alg / (timed_us * 1e-6) / 1e9:.0f} GB/s, measured "
         f"{(fetch + write) / (timed_us * 1e-6) / 1e9:.0f} GB/s, of {PEAK_HBM_GBS:.0f} GB/s HBM peak "
-        f"(roofline bound: {roofline_bound(w)}).",
+        f"(roofline bound: {roofline_bound(w)}"
+        + (f"; {buffer_sets(w)} buffer sets rotated" if roofline_bound(w) == "hbm" else "") + ").",
         "",
         f"Kernel source sha256 {rec['source_sha256'][:16]}...; bench.py reports this traffic only while it matches.",
         "",
@@ -211,6 +364,12 @@ def roofline_bound(w) -> str:
     dtype's matrix peak and the HBM peak, 'hbm' below it."""
     ridge = PEAK_TFLOPS[w.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
     return "mfma" if w.flops() / algorithmic_bytes(w) >= ridge else "hbm"
+
+
+def buffer_sets(w) -> int:
+    """Buffer sets rotated through for an HBM-bound workload: at least 3, and
+    more than 256 MB of inputs and outputs in all."""
+    return max(3, (512 << 20) // algorithmic_bytes(w) + 1)
 
 
 def algorithmic_bytes(w) -> int:
@@ -269,11 +428,8 @@ def cpu_baseline(w, q, k, v, mask, target_s: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the default warm-up (about 50 ms of work) lets the clocks settle after
-    # the power dip that follows the first launches of a busy kernel, so the
-    # timed steps measure the sustained rate
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="causal_bf16_d128_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -282,6 +438,9 @@ def main():
                          "scales the FETCH_SIZE / WRITE_SIZE counters), then exit")
     ap.add_argument("--summarize", metavar="PROF_DIR", default=None,
                     help="only write profiles/<workload>.md from rocprofv3 outputs under PROF_DIR, then exit")
+    ap.add_argument("--profile", metavar="PROF_DIR", default=None,
+                    help="run every rocprofv3 pass of the workload's profile into PROF_DIR (as child "
+                         "processes), then write profiles/<workload>.md")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -291,24 +450,13 @@ def main():
 
     import workloads as W
 
-    if args.summarize:
+    if args.summarize or args.profile:
         w = find_workload(W, args.workload)
-        base = f"--workload {w.name}" if w.name != "causal_bf16_d128_8k" else ""
-        cmds = {
-            "copy_mib": 1024,
-            "steps": args.steps,
-            "trace": f"rocprofv3 --kernel-trace --stats --output-format csv -d {args.summarize}/trace -o trace -- "
-                     f"python3 bench.py --steps {args.steps} --warmup {args.warmup} {base}".strip(),
-            "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {args.summarize}/fetch -o fetch -- "
-                     f"python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline {base}".strip(),
-            "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {args.summarize}/write -o write -- "
-                     f"python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline {base}".strip(),
-            "copyf": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {args.summarize}/copyf -o copyf -- "
-                     "python3 bench.py --copy-calibration-mib 1024",
-            "copyw": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {args.summarize}/copyw -o copyw -- "
-                     "python3 bench.py --copy-calibration-mib 1024",
-        }
-        summarize(args.summarize, w, cmds)
+        prof_dir = args.summarize or args.profile
+        if args.profile:
+            run_profile(prof_dir, w)
+        else:
+            summarize(prof_dir, w, profile_commands(prof_dir, w))
         return
 
     import torch
@@ -332,35 +480,49 @@ def main():
     log(f"workload: {w.name}: {w.note}")
 
     q, k, v, mask = W.draw(w)
-    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    md = None if mask is None else mask.to(dev)
-    out = None
-    if w.token_major_out:
-        out = torch.empty((w.B, w.qL, w.Hq, w.D), dtype=q.dtype, device=dev).transpose(1, 2)
-    else:
-        out = torch.empty((w.B, w.Hq, w.qL, w.D), dtype=q.dtype, device=dev)
-    lse = torch.empty((w.B, w.Hq, w.qL), dtype=torch.float32, device=dev)
+    bound = roofline_bound(w)
+    # A workload bound by HBM is timed over several buffer sets in turn, more
+    # than 256 MB in all, so that no launch finds its inputs in the 256 MB
+    # Infinity Cache (MALL) or the L2 from the launch before.
+    n_sets = buffer_sets(w) if bound == "hbm" else 1
     stream = torch.cuda.current_stream(dev)
+    sets = []
+    for _ in range(n_sets):
+        out = (torch.empty((w.B, w.qL, w.Hq, w.D), dtype=q.dtype, device=dev).transpose(1, 2) if w.token_major_out
+               else torch.empty((w.B, w.Hq, w.qL, w.D), dtype=q.dtype, device=dev))
+        sets.append((q.to(dev), k.to(dev), v.to(dev), None if mask is None else mask.to(dev), out,
+                     torch.empty((w.B, w.Hq, w.qL), dtype=torch.float32, device=dev)))
+    if n_sets > 1:
+        log(f"rotating {n_sets} buffer sets, {n_sets * algorithmic_bytes(w) / 1e6:.0f} MB of inputs and outputs")
 
-    def step():
+    def step(i):
+        qd, kd, vd, md, out, lse = sets[i % n_sets]
         fa.fwd(qd, kd, vd, mask=md, causal=w.causal, scale=w.scale, out=out, lse=lse, stream=stream,
                dropout_p=w.dropout_p, seed=w.seed, window=w.window)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    # per-launch kernel durations from HIP events on the launch stream, for
+    # the warm-up launches too (they show how the clock settles)
+    def events(n):
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
-    # per-launch kernel durations from HIP events on the launch stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    wev = events(args.warmup)
+    for i, (a, b) in enumerate(wev):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    evs = events(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, b in evs:
+    for i, (a, b) in enumerate(evs):
         a.record(stream)
-        step()
+        step(args.warmup + i)
         b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms = [a.elapsed_time(b) for a, b in evs]
+    warm_ms = [a.elapsed_time(b) for a, b in wev]
+    log("per-launch us, warm-up: " + " ".join(f"{x * 1e3:.0f}" for x in warm_ms))
+    log("per-launch us, timed:   " + " ".join(f"{x * 1e3:.0f}" for x in kern_ms))
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
     ms_per_step = wall * 1e3 / args.steps
 
@@ -379,7 +541,6 @@ def main():
         cpu = cpu_baseline(w, q, k, v, mask, args.cpu_seconds)
         log(f"cpu baseline: {cpu}")
 
-    bound = roofline_bound(w)
     gbs = nbytes / (kern_avg_ms * 1e-3) / 1e9
     if bound == "mfma":
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",

@@ -21,13 +21,16 @@ LIB = os.path.join(PKG, "libfa_mi355x.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_fwd_f32.hip"]
+# One translation unit per (dtype, head dim), so the library compiles in
+# parallel, plus the C ABI.
+HEAD_DIMS = (16, 32, 48, 64, 80, 96, 128, 256)
+SOURCES = ["fa_api.cpp", *[f"fa_fwd_bf16_d{d}.hip" for d in HEAD_DIMS], *[f"fa_fwd_f32_d{d}.hip" for d in HEAD_DIMS]]
 
 # Per-source code generation options.  The bf16 kernels keep every matrix
 # accumulator in ordinary VGPRs: their softmax works on the score
 # accumulators with vector instructions, and for D = 256 the default (AGPR)
 # form makes the register allocator shuffle accumulators and spill.
-SOURCE_FLAGS = {"fa_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+SOURCE_FLAGS = {f"fa_fwd_bf16_d{d}.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"] for d in HEAD_DIMS}
 
 
 def hipcc() -> str:
@@ -56,7 +59,7 @@ def _compile(src: str, extra=()) -> str:
 
 def build(verbose: bool = False, extra=()) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]

@@ -14,8 +14,82 @@
 #include <cstdio>
 #include <cstring>
 
+#include <mutex>
+#include <vector>
+
 #include "fa_common.h"
 #include "fa_mi355x.h"
+
+namespace fa {
+
+namespace {
+
+// The per-head-dim tables of one kind, concatenated once.
+typedef const Variant* (*TableFn)(int*);
+const Variant* concat_tables(const TableFn* fns, int nfns, std::vector<Variant>& all, std::once_flag& once, int* n)
+{
+    std::call_once(once, [&]() {
+        for (int i = 0; i < nfns; ++i) {
+            int k = 0;
+            const Variant* t = fns[i](&k);
+            all.insert(all.end(), t, t + k);
+        }
+    });
+    *n = (int)all.size();
+    return all.data();
+}
+
+}  // namespace
+
+#define FA_TABLE_OF(KIND)                                               \
+    const Variant* variants_##KIND(int* n)                              \
+    {                                                                   \
+        static const TableFn fns[] = {                                  \
+            variants_##KIND##_d16, variants_##KIND##_d32,  variants_##KIND##_d48, variants_##KIND##_d64, \
+            variants_##KIND##_d80, variants_##KIND##_d96, variants_##KIND##_d128, variants_##KIND##_d256}; \
+        static std::vector<Variant> all;                                \
+        static std::once_flag once;                                     \
+        return concat_tables(fns, 8, all, once, n);                     \
+    }
+FA_TABLE_OF(bf16)
+FA_TABLE_OF(f32)
+FA_TABLE_OF(bf16_dropout)
+FA_TABLE_OF(f32_dropout)
+#undef FA_TABLE_OF
+
+// Partials of split launches come from a stream-ordered memory pool that the
+// library creates for itself, one per device.  The process-wide default pool
+// and its attributes are left alone.  This pool keeps up to kPoolKeepBytes of
+// freed memory for reuse instead of returning it at every synchronisation.
+hipError_t library_pool(hipMemPool_t* out)
+{
+    constexpr uint64_t kPoolKeepBytes = 256ull << 20;
+    constexpr int kMaxDevices = 64;
+    static std::once_flag once[kMaxDevices];
+    static hipMemPool_t pools[kMaxDevices];
+    static hipError_t status[kMaxDevices];
+    int dev = 0;
+    const hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(once[dev], [dev]() {
+        hipMemPoolProps props;
+        std::memset(&props, 0, sizeof(props));
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        status[dev] = hipMemPoolCreate(&pools[dev], &props);
+        if (status[dev] == hipSuccess) {
+            uint64_t keep = kPoolKeepBytes;
+            status[dev] = hipMemPoolSetAttribute(pools[dev], hipMemPoolAttrReleaseThreshold, &keep);
+        }
+    });
+    *out = pools[dev];
+    return status[dev];
+}
+
+}  // namespace fa
 
 namespace {
 
@@ -77,23 +151,39 @@ const char* fa_last_error(void) { return g_last_error; }
 
 int fa_abi_version(void) { return FA_ABI_VERSION; }
 
+// Every compiled variant: the bf16 and fp32 tables, then their dropout tables.
+static const fa::Variant* variant_table(int which, int* n)
+{
+    switch (which) {
+    case 0: return fa::variants_bf16(n);
+    case 1: return fa::variants_f32(n);
+    case 2: return fa::variants_bf16_dropout(n);
+    case 3: return fa::variants_f32_dropout(n);
+    }
+    *n = 0;
+    return nullptr;
+}
+
 int fa_variant_count(void)
 {
-    int nb = 0, nf = 0;
-    fa::variants_bf16(&nb);
-    fa::variants_f32(&nf);
-    return nb + nf;
+    int total = 0;
+    for (int w = 0; w < 4; ++w) {
+        int n = 0;
+        variant_table(w, &n);
+        total += n;
+    }
+    return total;
 }
 
 const char* fa_variant_name(int i)
 {
-    int nb = 0, nf = 0;
-    const fa::Variant* tb = fa::variants_bf16(&nb);
-    const fa::Variant* tf = fa::variants_f32(&nf);
     if (i < 0) return nullptr;
-    if (i < nb) return tb[i].name;
-    i -= nb;
-    if (i < nf) return tf[i].name;
+    for (int w = 0; w < 4; ++w) {
+        int n = 0;
+        const fa::Variant* t = variant_table(w, &n);
+        if (i < n) return t[i].name;
+        i -= n;
+    }
     return nullptr;
 }
 

@@ -189,10 +189,26 @@ struct Variant {
     LaunchFn launch;
 };
 
-// Variant tables defined by each kernel translation unit (host only).
+// The head dims with compiled kernels; each has a translation unit per
+// dtype (fa_fwd_bf16_d<D>.hip, fa_fwd_f32_d<D>.hip) defining its variant
+// tables (host only).
+#define FA_FOR_EACH_HEAD_DIM(X) X(16) X(32) X(48) X(64) X(80) X(96) X(128) X(256)
+#define FA_DECLARE_TABLES(D)                      \
+    const Variant* variants_bf16_d##D(int* n);         \
+    const Variant* variants_bf16_dropout_d##D(int* n); \
+    const Variant* variants_f32_d##D(int* n);          \
+    const Variant* variants_f32_dropout_d##D(int* n);
+FA_FOR_EACH_HEAD_DIM(FA_DECLARE_TABLES)
+#undef FA_DECLARE_TABLES
+
+// Every variant of one kind, over all head dims (fa_api.cpp, host only).
 const Variant* variants_bf16(int* n);
 const Variant* variants_f32(int* n);
 const Variant* variants_bf16_dropout(int* n);
 const Variant* variants_f32_dropout(int* n);
+
+// The stream-ordered memory pool the library creates for itself on the
+// current device (fa_api.cpp): split launches take their partials from it.
+hipError_t library_pool(hipMemPool_t* out);
 
 }  // namespace fa

@@ -1,4 +1,7 @@
-// fa_fwd_bf16.hip - FlashAttention-2 forward, bf16 in/out, for gfx950.
+// fa_fwd_bf16.h - FlashAttention-2 forward, bf16 in/out, for gfx950: the
+// kernel templates and their launchers.  Each fa_fwd_bf16_d<D>.hip
+// instantiates the variants of one head dim (so the library compiles in
+// parallel).
 //
 // What is computed (mlx-native flash_attn_train.rs, module doc "Algorithm";
 // oxibonsai dit_attention_flash.rs, module doc "Flash-attention v2
@@ -46,10 +49,13 @@
 //   * Ragged tails: query rows past qL load zeros and are not stored; key
 //     rows past kL repeat row kL - 1 (finite values) and their scores are
 //     masked to -inf.
+#pragma once
+
 #include "fa_common.h"
 
 #include <math.h>
 
+#include <cstring>
 #include <mutex>
 #include <type_traits>
 
@@ -810,27 +816,6 @@ __global__ void __launch_bounds__(256) merge_splits_bf16_kernel(const FwdParams 
     if (lane == 0) p.lse[row] = (sum > 0.f) ? lmax + __builtin_amdgcn_logf(sum) * kLn2 : 0.f;
 }
 
-// The device's default stream-ordered memory pool keeps up to this much
-// freed memory for reuse instead of returning it at every synchronisation
-// (split launches allocate their partials from it).
-constexpr uint64_t kPoolKeepBytes = 256ull << 20;
-
-inline hipError_t keep_pool_memory()
-{
-    static std::once_flag once[64];
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err != hipSuccess || dev < 0 || dev >= 64) return err;
-    std::call_once(once[dev], [&]() {
-        hipMemPool_t pool;
-        if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
-            uint64_t keep = kPoolKeepBytes;
-            hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
-        }
-    });
-    return hipSuccess;
-}
-
 // Work-groups of the work-group kernel one CU holds: by waves per SIMD, and
 // by LDS (tiles padded to 1 KiB blocks, NB buffers each for K and V).
 template <int D, int NW, int BN, int WPE, int NB>
@@ -867,6 +852,8 @@ int split_plan(const FwdParams& p, int64_t wgs, int wgs_per_cu_, int* split_tile
 template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB, bool DROP = false>
 hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
 {
+    // the work-group kernel divides its grid index by n_split
+    if (p.n_split < 1) return hipErrorInvalidValue;
     constexpr int kWgsPerCu = wgs_per_cu<D, NW, BN, WPE, NB>();
     FwdParams q = p;
     const int64_t wgs = p.head_pack ? (int64_t)p.n_qtiles * ((p.group + NW - 1) / NW) * p.Hkv * p.B
@@ -879,13 +866,14 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
                            dim3(NW * 64), 0, st, q);
         return hipGetLastError();
     }
-    // partials from the stream-ordered pool: freed (for reuse by later calls
-    // on this stream) once the merge has read them
+    // partials from the library's stream-ordered pool: freed (for reuse by
+    // later calls on this stream) once the merge has read them
     const int64_t rows = (int64_t)p.B * p.Hq * p.qL;
     void* ws = nullptr;
-    hipError_t err = keep_pool_memory();
+    hipMemPool_t pool;
+    hipError_t err = library_pool(&pool);
     if (err != hipSuccess) return err;
-    err = hipMallocAsync(&ws, (size_t)n_split * rows * (D + 1) * sizeof(float), st);
+    err = hipMallocFromPoolAsync(&ws, (size_t)n_split * rows * (D + 1) * sizeof(float), pool, st);
     if (err != hipSuccess) return err;
     q.o_part = (float*)ws;
     q.l_part = q.o_part + (int64_t)n_split * rows * D;
@@ -1420,7 +1408,7 @@ constexpr int kShortQueries = 64;
 template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB>
 hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
 {
-    // the work-group kernel divides its grid index by n_split
+    // (the work-group launcher rejects n_split < 1; the other kernels ignore it)
     if (p.n_split < 1) return hipErrorInvalidValue;
     if constexpr (D == 128) {
         // Short key ranges are HBM-bound (Q in, O out).
@@ -1551,24 +1539,6 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
     FA_BF16_VARIANT_CFG(D, MASK_BOOL, false, "fwd_bf16_d" #D "_bool", MCFG),              \
     FA_BF16_VARIANT_CFG(D, MASK_BOOL, true, "fwd_bf16_d" #D "_bool_causal", MCFG)
 
-// Host-only accessor: a namespace-scope const table would also be emitted
-// for the device, where the launch functions do not exist.
-const Variant* variants_bf16(int* n)
-{
-    static const Variant table[] = {
-    FA_BF16_FOR_D(16, FA_BF16_D16_CFG, FA_BF16_D16_MASKED_CFG),
-    FA_BF16_FOR_D(32, FA_BF16_D32_CFG, FA_BF16_D32_MASKED_CFG),
-    FA_BF16_FOR_D(48, FA_BF16_D48_CFG, FA_BF16_D48_MASKED_CFG),
-    FA_BF16_FOR_D(64, FA_BF16_D64_CFG, FA_BF16_D64_MASKED_CFG),
-    FA_BF16_FOR_D(80, FA_BF16_D80_CFG, FA_BF16_D80_MASKED_CFG),
-    FA_BF16_FOR_D(96, FA_BF16_D96_CFG, FA_BF16_D96_MASKED_CFG),
-    FA_BF16_FOR_D(128, FA_BF16_D128_CFG, FA_BF16_D128_MASKED_CFG),
-    FA_BF16_FOR_D(256, FA_BF16_D256_CFG, FA_BF16_D256_MASKED_CFG),
-};
-    *n = (int)(sizeof(table) / sizeof(table[0]));
-    return table;
-}
-
 // Dropout variants: the work-group kernel at the head dims' own launch
 // shapes (no short-key or short-query special cases).
 #define FA_BF16_DROP_VARIANT(D, MASK, CAUSAL, NAME, NW, BN, WPE, SCHED, NB) \
@@ -1581,21 +1551,5 @@ const Variant* variants_bf16(int* n)
     FA_BF16_DROP_VARIANT_CFG(D, MASK_ADD, true, "fwd_bf16_d" #D "_additive_causal_dropout", MCFG), \
     FA_BF16_DROP_VARIANT_CFG(D, MASK_BOOL, false, "fwd_bf16_d" #D "_bool_dropout", MCFG),          \
     FA_BF16_DROP_VARIANT_CFG(D, MASK_BOOL, true, "fwd_bf16_d" #D "_bool_causal_dropout", MCFG)
-
-const Variant* variants_bf16_dropout(int* n)
-{
-    static const Variant table[] = {
-    FA_BF16_DROP_FOR_D(16, FA_BF16_D16_CFG, FA_BF16_D16_MASKED_CFG),
-    FA_BF16_DROP_FOR_D(32, FA_BF16_D32_CFG, FA_BF16_D32_MASKED_CFG),
-    FA_BF16_DROP_FOR_D(48, FA_BF16_D48_CFG, FA_BF16_D48_MASKED_CFG),
-    FA_BF16_DROP_FOR_D(64, FA_BF16_D64_CFG, FA_BF16_D64_MASKED_CFG),
-    FA_BF16_DROP_FOR_D(80, FA_BF16_D80_CFG, FA_BF16_D80_MASKED_CFG),
-    FA_BF16_DROP_FOR_D(96, FA_BF16_D96_CFG, FA_BF16_D96_MASKED_CFG),
-    FA_BF16_DROP_FOR_D(128, FA_BF16_D128_CFG, FA_BF16_D128_MASKED_CFG),
-    FA_BF16_DROP_FOR_D(256, FA_BF16_D256_CFG, FA_BF16_D256_MASKED_CFG),
-};
-    *n = (int)(sizeof(table) / sizeof(table[0]));
-    return table;
-}
 
 }  // namespace fa

@@ -1,4 +1,6 @@
-// fa_fwd_f32.hip - FlashAttention-2 forward, fp32 in/out, for gfx950.
+// fa_fwd_f32.h - FlashAttention-2 forward, fp32 in/out, for gfx950: the
+// kernel template and its launcher.  Each fa_fwd_f32_d<D>.hip instantiates
+// the variants of one head dim.
 //
 // Same algorithm as the bf16 kernel (mlx-native flash_attn_train.rs, module
 // doc "Algorithm"), with every operand kept in fp32: Q, K, V, the scores, P
@@ -21,6 +23,8 @@
 //   * Output rows are written through the caller's strides, which is how the
 //     token-major [seq, heads*D] layout of the DiT joint attention
 //     (oxibonsai dit_attention_flash.rs, module doc) is produced in place.
+#pragma once
+
 #include "fa_common.h"
 
 #include <math.h>
@@ -395,24 +399,6 @@ hipError_t launch_f32(const FwdParams& p, hipStream_t st)
 // expands a CFG macro into separate arguments before FA_F32_FOR_D sees them
 #define FA_F32_FOR_D_CFG(D, ...) FA_F32_FOR_D(D, __VA_ARGS__)
 
-// Host-only accessor: a namespace-scope const table would also be emitted
-// for the device, where the launch functions do not exist.
-const Variant* variants_f32(int* n)
-{
-    static const Variant table[] = {
-    FA_F32_FOR_D_CFG(16, FA_F32_D16_CFG),
-    FA_F32_FOR_D_CFG(32, FA_F32_D32_CFG),
-    FA_F32_FOR_D_CFG(48, FA_F32_D48_CFG),
-    FA_F32_FOR_D_CFG(64, FA_F32_D64_CFG),
-    FA_F32_FOR_D_CFG(80, FA_F32_D80_CFG),
-    FA_F32_FOR_D_CFG(96, FA_F32_D96_CFG),
-    FA_F32_FOR_D_CFG(128, FA_F32_D128_CFG),
-    FA_F32_FOR_D_CFG(256, FA_F32_D256_CFG),
-};
-    *n = (int)(sizeof(table) / sizeof(table[0]));
-    return table;
-}
-
 // Dropout variants: the same kernel at the same launch shapes, with the
 // multipliers applied to the fp32 P before P V.
 #define FA_F32_DROP_VARIANT(D, MASK, CAUSAL, NW, BN, NAME) \
@@ -425,21 +411,5 @@ const Variant* variants_f32(int* n)
     FA_F32_DROP_VARIANT(D, MASK_BOOL, false, NW, BN, "fwd_f32_d" #D "_bool_dropout"),          \
     FA_F32_DROP_VARIANT(D, MASK_BOOL, true, NW, BN, "fwd_f32_d" #D "_bool_causal_dropout")
 #define FA_F32_DROP_FOR_D_CFG(D, ...) FA_F32_DROP_FOR_D(D, __VA_ARGS__)
-
-const Variant* variants_f32_dropout(int* n)
-{
-    static const Variant table[] = {
-    FA_F32_DROP_FOR_D_CFG(16, FA_F32_D16_CFG),
-    FA_F32_DROP_FOR_D_CFG(32, FA_F32_D32_CFG),
-    FA_F32_DROP_FOR_D_CFG(48, FA_F32_D48_CFG),
-    FA_F32_DROP_FOR_D_CFG(64, FA_F32_D64_CFG),
-    FA_F32_DROP_FOR_D_CFG(80, FA_F32_D80_CFG),
-    FA_F32_DROP_FOR_D_CFG(96, FA_F32_D96_CFG),
-    FA_F32_DROP_FOR_D_CFG(128, FA_F32_D128_CFG),
-    FA_F32_DROP_FOR_D_CFG(256, FA_F32_D256_CFG),
-};
-    *n = (int)(sizeof(table) / sizeof(table[0]));
-    return table;
-}
 
 }  // namespace fa

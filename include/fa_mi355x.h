@@ -25,13 +25,16 @@
  *     owns all of them.  Q, K, V and the mask are read-only; O and L are
  *     overwritten in full (rows beyond qL and padding are never touched).
  *   - The call enqueues work on `hip_stream` (a hipStream_t; NULL = the null
- *     stream) and returns without synchronising.  One case uses device
- *     memory of its own: a bf16 call whose grid of query tiles leaves most
+ *     stream) and returns without synchronising.
+ *   - Allocation: the forward path allocates no device memory, with one
+ *     stated exception.  A bf16 call whose grid of query tiles leaves most
  *     CUs idle while its key range is long splits that range over
- *     work-groups.  It then takes fp32 partials (n_split * B * H_q * qL *
- *     (D + 1) * 4 bytes) from the device's default stream-ordered memory
- *     pool on `hip_stream` and returns them to the pool on the same stream
- *     after the merge.  Every other call allocates nothing.
+ *     work-groups, and takes fp32 partials (n_split * B * H_q * qL * (D + 1)
+ *     * 4 bytes) from a stream-ordered memory pool that the library creates
+ *     for itself on each device (hipMemPoolCreate; it keeps up to 256 MiB of
+ *     freed memory for reuse).  They are returned to that pool on
+ *     `hip_stream` after the merge.  The device's default pool and every
+ *     other process-wide allocator setting are left untouched.
  *   - All argument checks run before any launch: a failed check writes
  *     nothing, launches nothing and returns FA_ERR_INVALID_ARGUMENT (or
  *     FA_ERR_UNSUPPORTED for a valid combination that is not built), with a
@@ -167,7 +170,8 @@ fa_status fa_fwd_window(const void* Q, const void* K, const void* V, const void*
 /* 1 if (dtype, D, mask_kind, causal) has a compiled kernel, else 0. */
 int fa_supported(fa_dtype dtype, int D, fa_mask_kind mask_kind, int causal);
 
-/* Number of compiled kernel variants, and the name of variant i (NULL past
+/* Number of compiled kernel variants -- every (dtype, D, mask kind, causal)
+ * of fa_fwd, then of fa_fwd_dropout -- and the name of variant i (NULL past
  * the end); the names are static strings (cf. the kernel-name lists that
  * mlx-native flash_attn_train.rs exposes to its tests). */
 int fa_variant_count(void);

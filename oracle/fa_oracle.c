@@ -63,10 +63,10 @@
  * (offset + floor(n / 4), 64-bit, low word first; then two zero words)
  * under the 64-bit key `seed` (low word first); word n mod 4 of the result,
  * w, gives u = floor(w / 2^8) / 2^24.
- * The generator's output stream is pinned by its properties only (a
- * bijection per key, uniform words, the keep rate); no independent
- * implementation of Philox-4x32 is available here: parity unpinned for the
- * exact stream.
+ * The generator and the position-to-word map are pinned exactly against
+ * rocRAND's independent host implementation of Philox-4x32-10 (whole blocks
+ * at arbitrary counters and keys, and the word at stream position n with the
+ * carry from the low counter word into the high one).
  */
 #include <math.h>
 #include <stdint.h>

@@ -50,7 +50,10 @@ def test_version_and_status_strings(lib):
 
 def test_variant_table_covers_every_combination(lib):
     names = [fa.fa_variant_name(i) for i in range(fa.fa_variant_count())]
-    assert None not in names and len(set(names)) == len(names) == 96
+    # every (dtype, D, mask kind, causal) for fa_fwd and again for fa_fwd_dropout
+    assert None not in names and len(set(names)) == len(names) == 192
+    dropout = [n for n in names if n.endswith("_dropout")]
+    assert len(dropout) == 96 and {n[:-len("_dropout")] for n in dropout} == set(names) - set(dropout)
     assert fa.fa_variant_name(len(names)) is None and fa.fa_variant_name(-1) is None
     for dt in (fa.FA_DTYPE_F32, fa.FA_DTYPE_BF16):
         for D in (16, 32, 48, 64, 80, 96, 128, 256):

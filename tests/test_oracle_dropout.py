@@ -2,10 +2,10 @@
 `keep_global`, the `dropout` branch of `forward_flash`) and of its generator,
 Philox-4x32-10 (Salmon, Moraes, Dror and Shaw, SC 2011).
 
-The exact output stream of the generator has no independent implementation
-here to compare with, so it is pinned by properties a wrong constant, a
-dropped key step or a swapped word would break (a bijection per key, uniform
-and independent-looking words, full avalanche, the keep rate).  The dropout
+The generator's exact output stream is pinned against rocRAND in
+test_oracle_philox.py; the properties checked here (a bijection per key,
+uniform and independent-looking words, full avalanche, the keep rate) are a
+second line of defence.  The dropout
 semantics are pinned exactly: p = 0 and p = 1, L unchanged, a pure-Python
 evaluation of sum_j softmax_ij k_ij / (1 - p) V_j at the oracle's positions
 n = ((b*Hq + h)*qL + i)*kL + j, and unbiasedness over seeds.
