@@ -231,7 +231,7 @@ def summarize(prof_dir, w, commands):
             cyc = d["GRBM_GUI_ACTIVE"] / N_XCD  # GPU cycles of the dispatch
             return {"us": ns / 1e3, "ghz": cyc / ns, "cycles": cyc,
                     "mfma_busy": d["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * cyc),
-                    "cu_busy": 4 * d["SQ_BUSY_CU_CYCLES"] / (N_CU * cyc),
+                    "cu_busy": d["SQ_BUSY_CU_CYCLES"] / (N_CU * cyc),
                     "valu_per_wave": d["SQ_INSTS_VALU"] / max(1.0, d["SQ_WAVES"]),
                     "trans_per_wave": d["SQ_INSTS_VALU_TRANS_F32"] / max(1.0, d["SQ_WAVES"]),
                     "mfma_flop": d[mops] * 512,
@@ -249,7 +249,7 @@ def summarize(prof_dir, w, commands):
             "```",
             "",
             f"Clock = GRBM_GUI_ACTIVE / {N_XCD} XCDs / dispatch time; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
-            f"({N_SIMD} SIMDs x cycles); CU busy = 4 SQ_BUSY_CU_CYCLES / ({N_CU} CUs x cycles); matrix FLOP = "
+            f"({N_SIMD} SIMDs x cycles); CU busy = SQ_BUSY_CU_CYCLES / ({N_CU} CUs x cycles); matrix FLOP = "
             f"{mops} x 512; LDS conflict = SQ_LDS_BANK_CONFLICT / ({N_CU} CUs x cycles).  Timings under --pmc "
             "are serialised dispatches, so they differ from the trace above.",
             "",

@@ -67,6 +67,26 @@
  * rocRAND's independent host implementation of Philox-4x32-10 (whole blocks
  * at arbitrary counters and keys, and the word at stream position n with the
  * carry from the low counter word into the high one).
+ *
+ * Backward pass (fa_oracle_bwd; forge flash_attention_mma.metal, the
+ * backward section's header and kernels flash_attn_bwd_dq_mma,
+ * flash_attn_bwd_dv_mma and flash_attn_bwd_dk_mma; mlx-native
+ * flash_attn_train.rs, "Phase 2 -- FA-2 backward kernel"; ruDNN
+ * dense_attention.rs, `backward_kv_owned`): for an upstream gradient dO of
+ * the output O, with P_ij the softmax weights of the forward pass (0 for
+ * keys that are not allowed), the gradients are the chain rule through
+ * O = P V and the row softmax, written out plainly:
+ *
+ *     dP_ij    = dO_i . V_j
+ *     dS_ij    = P_ij (dP_ij - sum_k P_ik dP_ik)     (the softmax Jacobian)
+ *     dQ_i     = scale sum_j dS_ij K_j
+ *     dK_j     = scale sum_{h in j's group, i} dS_ij Q_i
+ *     dV_j     = sum_{h in j's group, i} P_ij dO_i
+ *
+ * The row sum sum_k P_ik dP_ik is taken from the weights themselves (the
+ * definition), not through the identity rowsum(dO_i * O_i) the kernels use.
+ * A row with no allowed key contributes nothing.  The mask is an input
+ * constant: no gradient is formed for it.
  */
 #include <math.h>
 #include <stdint.h>
@@ -270,4 +290,169 @@ int fa_oracle_fwd_dropout(const double* Q, const double* K, const double* V,
     if (!(p >= 0.0f && p <= 1.0f)) return -1;
     const dropout_t drop = {1, p, seed, offset};
     return run_rows(Q, K, V, mask, mask_kind, B, Hq, Hkv, qL, kL, D, scale, causal, 0, rows, nrows, O, L, &drop);
+}
+
+/* ------------------------------------------------------------------ backward */
+
+/* The score s_ij and whether key j is allowed for query row `flat` (the same
+ * rules as one_row: causal top-left, bool mask, additive mask, -inf). */
+static double score_of(const double* Q, const double* K, const double* mask, int mask_kind,
+                       int Hq, int Hkv, int qL, int kL, int D, double scale, int causal,
+                       int64_t flat, int64_t j, int* allowed)
+{
+    const int64_t i = flat % qL;
+    const int64_t bh = flat / qL;
+    const int64_t h = bh % Hq;
+    const int64_t b = bh / Hq;
+    const int64_t g = h / (Hq / Hkv);
+    /* keys excluded by position or by the bool mask need no score */
+    if ((causal && j > i) || (mask_kind == 2 && mask[flat * (int64_t)kL + j] == 0.0)) {
+        *allowed = 0;
+        return -INFINITY;
+    }
+    const double* q = Q + flat * D;
+    const double* k = K + ((b * Hkv + g) * (int64_t)kL + j) * D;
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d) dot += q[d] * k[d];
+    double sc = scale * dot;
+    if (mask_kind == 1) sc = sc + mask[flat * (int64_t)kL + j];
+    *allowed = sc != -INFINITY;
+    return sc;
+}
+
+/* dP_ij = dO_i . V_j */
+static double dp_of(const double* dO, const double* V, int Hq, int Hkv, int qL, int kL, int D,
+                    int64_t flat, int64_t j)
+{
+    const int64_t bh = flat / qL;
+    const int64_t h = bh % Hq;
+    const int64_t b = bh / Hq;
+    const int64_t g = h / (Hq / Hkv);
+    const double* go = dO + flat * D;
+    const double* v = V + ((b * Hkv + g) * (int64_t)kL + j) * D;
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d) dot += go[d] * v[d];
+    return dot;
+}
+
+/*
+ * fa_oracle_bwd - dQ, dK, dV of attention (see the header), fp64.
+ *
+ * Q, dO [B, Hq, qL, D]; K, V [B, Hkv, kL, D]; mask [B, Hq, qL, kL] or NULL.
+ * qrows: flat query rows (b*Hq + h)*qL + i whose dQ is wanted (NULL = all,
+ * in order), nq of them; dQ is [nq, D].
+ * krows: flat key rows (b*Hkv + g)*kL + j whose dK and dV are wanted (NULL =
+ * all), nk of them; dK and dV are [nk, D].
+ * Returns 0, or -1 when an argument is out of range.
+ */
+int fa_oracle_bwd(const double* Q, const double* K, const double* V, const double* dO,
+                  const double* mask, int mask_kind,
+                  int B, int Hq, int Hkv, int qL, int kL, int D,
+                  double scale, int causal,
+                  const int64_t* qrows, int64_t nq, const int64_t* krows, int64_t nk,
+                  double* dQ, double* dK, double* dV)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || qL <= 0 || kL <= 0 || D <= 0) return -1;
+    if (Hq % Hkv != 0) return -1;
+    if (mask_kind < 0 || mask_kind > 2) return -1;
+    if ((mask_kind != 0) != (mask != NULL)) return -1;
+    const int64_t total_q = (int64_t)B * Hq * qL;
+    const int64_t total_k = (int64_t)B * Hkv * kL;
+    if (qrows == NULL) nq = total_q;
+    if (krows == NULL) nk = total_k;
+    for (int64_t r = 0; r < nq && qrows; ++r)
+        if (qrows[r] < 0 || qrows[r] >= total_q) return -1;
+    for (int64_t r = 0; r < nk && krows; ++r)
+        if (krows[r] < 0 || krows[r] >= total_k) return -1;
+
+    /* 1. per query row: the softmax normaliser (as m and l) and the row sum
+     *    sum_k P_ik dP_ik, over the allowed keys */
+    double* row_m = (double*)malloc(sizeof(double) * (size_t)total_q);
+    double* row_l = (double*)malloc(sizeof(double) * (size_t)total_q);
+    double* row_pdp = (double*)malloc(sizeof(double) * (size_t)total_q);
+    if (!row_m || !row_l || !row_pdp) {
+        free(row_m);
+        free(row_l);
+        free(row_pdp);
+        return -1;
+    }
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < total_q; ++r) {
+        double m = -INFINITY;
+        for (int64_t j = 0; j < kL; ++j) {
+            int ok;
+            const double sc = score_of(Q, K, mask, mask_kind, Hq, Hkv, qL, kL, D, scale, causal, r, j, &ok);
+            if (ok && sc > m) m = sc;
+        }
+        double l = 0.0, pdp = 0.0;
+        if (m != -INFINITY) {
+            for (int64_t j = 0; j < kL; ++j) {
+                int ok;
+                const double sc = score_of(Q, K, mask, mask_kind, Hq, Hkv, qL, kL, D, scale, causal, r, j, &ok);
+                if (!ok) continue;
+                const double e = exp(sc - m);
+                l += e;
+                pdp += e * dp_of(dO, V, Hq, Hkv, qL, kL, D, r, j);
+            }
+            pdp /= l;
+        }
+        row_m[r] = m;
+        row_l[r] = l;
+        row_pdp[r] = pdp;
+    }
+
+    /* 2. dQ_i = scale sum_j dS_ij K_j */
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < nq; ++r) {
+        const int64_t flat = qrows ? qrows[r] : r;
+        const int64_t bh = flat / qL;
+        const int64_t b = bh / Hq;
+        const int64_t g = (bh % Hq) / (Hq / Hkv);
+        double* out = dQ + r * D;
+        for (int d = 0; d < D; ++d) out[d] = 0.0;
+        if (row_m[flat] == -INFINITY) continue;
+        for (int64_t j = 0; j < kL; ++j) {
+            int ok;
+            const double sc = score_of(Q, K, mask, mask_kind, Hq, Hkv, qL, kL, D, scale, causal, flat, j, &ok);
+            if (!ok) continue;
+            const double p = exp(sc - row_m[flat]) / row_l[flat];
+            const double ds = p * (dp_of(dO, V, Hq, Hkv, qL, kL, D, flat, j) - row_pdp[flat]);
+            const double* k = K + ((b * Hkv + g) * (int64_t)kL + j) * D;
+            for (int d = 0; d < D; ++d) out[d] += scale * ds * k[d];
+        }
+    }
+
+    /* 3. dK_j and dV_j: every query row of every head of key j's group */
+    const int64_t group = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < nk; ++r) {
+        const int64_t flat = krows ? krows[r] : r;
+        const int64_t j = flat % kL;
+        const int64_t bg = flat / kL;
+        const int64_t g = bg % Hkv;
+        const int64_t b = bg / Hkv;
+        double* gk = dK + r * D;
+        double* gv = dV + r * D;
+        for (int d = 0; d < D; ++d) gk[d] = gv[d] = 0.0;
+        for (int64_t h = g * group; h < (g + 1) * group; ++h)
+            for (int64_t i = 0; i < qL; ++i) {
+                const int64_t qf = (b * Hq + h) * qL + i;
+                if (row_m[qf] == -INFINITY) continue;
+                int ok;
+                const double sc = score_of(Q, K, mask, mask_kind, Hq, Hkv, qL, kL, D, scale, causal, qf, j, &ok);
+                if (!ok) continue;
+                const double p = exp(sc - row_m[qf]) / row_l[qf];
+                const double ds = p * (dp_of(dO, V, Hq, Hkv, qL, kL, D, qf, j) - row_pdp[qf]);
+                const double* q = Q + qf * D;
+                const double* go = dO + qf * D;
+                for (int d = 0; d < D; ++d) {
+                    gk[d] += scale * ds * q[d];
+                    gv[d] += p * go[d];
+                }
+            }
+    }
+    free(row_m);
+    free(row_l);
+    free(row_pdp);
+    return 0;
 }

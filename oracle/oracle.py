@@ -57,6 +57,12 @@ class OracleLib:
                                                           ctypes.c_uint64]
         self.lib.fa_oracle_dropout_multiplier.restype = ctypes.c_double
         self.lib.fa_oracle_threads.restype = ctypes.c_int
+        fb = self.lib.fa_oracle_bwd
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        fb.argtypes = [dp, dp, dp, dp, dp, ctypes.c_int,
+                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                       ctypes.c_double, ctypes.c_int, i64p, ctypes.c_int64, i64p, ctypes.c_int64, dp, dp, dp]
+        fb.restype = ctypes.c_int
 
     def threads(self) -> int:
         return int(self.lib.fa_oracle_threads())
@@ -130,6 +136,56 @@ class OracleLib:
         return O, L
 
 
+    def bwd(self, q, k, v, do, *, scale, causal=False, mask=None, mask_kind="none", qrows=None, krows=None):
+        """Gradients of the attention forward pass in fp64 (fa_oracle_bwd).
+
+        q, do [B,Hq,qL,D]; k, v [B,Hkv,kL,D]; mask as for fwd.  Returns
+        (dQ, dK, dV) in the input shapes, or dQ [len(qrows), D] for the flat
+        query rows (b*Hq + h)*qL + i and dK, dV [len(krows), D] for the flat
+        key rows (b*Hkv + g)*kL + j when those are given.
+        """
+        q, k, v, do = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v, do))
+        B, Hq, qL, D = q.shape
+        Bk, Hkv, kL, Dk = k.shape
+        if v.shape != k.shape or do.shape != q.shape or Bk != B or Dk != D:
+            raise ValueError("oracle: q/k/v/do shapes disagree")
+        kind = MASK_KINDS[mask_kind]
+        mptr = None
+        if kind != 0:
+            m = np.asarray(mask)
+            if kind == 2:
+                m = (m != 0).astype(np.float64)
+            m = np.ascontiguousarray(np.broadcast_to(m, (B, Hq, qL, kL)), dtype=np.float64)
+            mptr = m.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+        elif mask is not None:
+            raise ValueError("oracle: mask given with mask_kind='none'")
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        dp = ctypes.POINTER(ctypes.c_double)
+
+        def rows_arg(rows, total):
+            if rows is None:
+                return None, None, total
+            rows = np.ascontiguousarray(rows, dtype=np.int64)
+            return rows, rows.ctypes.data_as(i64p), rows.size
+
+        qr, qptr, nq = rows_arg(qrows, B * Hq * qL)
+        kr, kptr, nk = rows_arg(krows, B * Hkv * kL)
+        dQ = np.empty((nq, D))
+        dK = np.empty((nk, D))
+        dV = np.empty((nk, D))
+        rc = self.lib.fa_oracle_bwd(q.ctypes.data_as(dp), k.ctypes.data_as(dp), v.ctypes.data_as(dp),
+                                    do.ctypes.data_as(dp), mptr, kind, B, Hq, Hkv, qL, kL, D, float(scale),
+                                    int(bool(causal)), qptr, nq, kptr, nk, dQ.ctypes.data_as(dp),
+                                    dK.ctypes.data_as(dp), dV.ctypes.data_as(dp))
+        if rc != 0:
+            raise ValueError("oracle: fa_oracle_bwd rejected its arguments")
+        if qrows is None:
+            dQ = dQ.reshape(B, Hq, qL, D)
+        if krows is None:
+            dK, dV = dK.reshape(B, Hkv, kL, D), dV.reshape(B, Hkv, kL, D)
+        return dQ, dK, dV
+
+
 _DEFAULT = None
 
 
@@ -159,3 +215,10 @@ def dropout_multiplier(n, p, seed, offset=0):
 
 def oracle_threads() -> int:
     return _default().threads()
+
+
+def attention_bwd(q, k, v, do, *, scale, causal=False, mask=None, mask_kind="none", qrows=None, krows=None):
+    """fp64 gradients dQ, dK, dV of the attention forward pass for the upstream
+    gradient do, with the default compiled oracle (see OracleLib.bwd)."""
+    return _default().bwd(q, k, v, do, scale=scale, causal=causal, mask=mask, mask_kind=mask_kind, qrows=qrows,
+                          krows=krows)
