@@ -302,22 +302,22 @@ static double score_of(const double* Q, const double* K, const double* mask, int
 {
     const int64_t i = flat % qL;
     const int64_t bh = flat / qL;
-    const int64_t h = bh % Hq;
+    const int64_t head = bh % Hq;
     const int64_t b = bh / Hq;
-    const int64_t g = h / (Hq / Hkv);
+    const int64_t g = head / (Hq / Hkv);
     /* keys excluded by position or by the bool mask need no score */
     if ((causal && j > i) || (mask_kind == 2 && mask[flat * (int64_t)kL + j] == 0.0)) {
         *allowed = 0;
         return -INFINITY;
     }
-    const double* q = Q + flat * D;
-    const double* k = K + ((b * Hkv + g) * (int64_t)kL + j) * D;
+    const double* qrow = Q + flat * D;
+    const double* krow = K + ((b * Hkv + g) * (int64_t)kL + j) * D;
     double dot = 0.0;
-    for (int d = 0; d < D; ++d) dot += q[d] * k[d];
-    double sc = scale * dot;
-    if (mask_kind == 1) sc = sc + mask[flat * (int64_t)kL + j];
-    *allowed = sc != -INFINITY;
-    return sc;
+    for (int d = 0; d < D; ++d) dot += qrow[d] * krow[d];
+    double score = scale * dot;
+    if (mask_kind == 1) score = score + mask[flat * (int64_t)kL + j];
+    *allowed = score != -INFINITY;
+    return score;
 }
 
 /* dP_ij = dO_i . V_j */
@@ -325,9 +325,9 @@ static double dp_of(const double* dO, const double* V, int Hq, int Hkv, int qL, 
                     int64_t flat, int64_t j)
 {
     const int64_t bh = flat / qL;
-    const int64_t h = bh % Hq;
+    const int64_t head = bh % Hq;
     const int64_t b = bh / Hq;
-    const int64_t g = h / (Hq / Hkv);
+    const int64_t g = head / (Hq / Hkv);
     const double* go = dO + flat * D;
     const double* v = V + ((b * Hkv + g) * (int64_t)kL + j) * D;
     double dot = 0.0;

@@ -201,8 +201,8 @@ BWD_MUTANTS = {
                   "            for (int d = 0; d < D; ++d) out[d] += scale * ds * k[d];"),
     "causal_off_by_one": ("if ((causal && j > i) || (mask_kind == 2", "if ((causal && j >= i) || (mask_kind == 2"),
     "group_one_head": ("for (int64_t h = g * group; h < (g + 1) * group; ++h)", "for (int64_t h = g; h < g + 1; ++h)"),
-    "mask_subtracted": ("    if (mask_kind == 1) sc = sc + mask[flat * (int64_t)kL + j];\n    *allowed",
-                        "    if (mask_kind == 1) sc = sc - mask[flat * (int64_t)kL + j];\n    *allowed"),
+    "mask_subtracted": ("if (mask_kind == 1) score = score + mask[flat * (int64_t)kL + j];",
+                        "if (mask_kind == 1) score = score - mask[flat * (int64_t)kL + j];"),
     "dq_sign": ("for (int d = 0; d < D; ++d) out[d] += scale * ds * k[d];",
                 "for (int d = 0; d < D; ++d) out[d] -= scale * ds * k[d];"),
 }
