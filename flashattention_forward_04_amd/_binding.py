@@ -18,8 +18,8 @@ FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_DTYPE_F32, FA_DTYPE_BF16 = 0, 1
 FA_MASK_NONE, FA_MASK_ADDITIVE, FA_MASK_BOOL = 0, 1, 2
 
-EXPORTS = ("fa_fwd", "fa_fwd_strided", "fa_fwd_dropout", "fa_fwd_window", "fa_supported", "fa_variant_count", "fa_variant_name",
-           "fa_status_string", "fa_last_error", "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_strided", "fa_fwd_strided_noalloc", "fa_fwd_dropout", "fa_fwd_window", "fa_supported",
+           "fa_variant_count", "fa_variant_name", "fa_status_string", "fa_last_error", "fa_abi_version")
 
 
 class FaError(RuntimeError):
@@ -53,6 +53,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, i32,
                                    ctypes.POINTER(FaStrides), vp]
     lib.fa_fwd_strided.restype = i32
+    lib.fa_fwd_strided_noalloc.argtypes = list(lib.fa_fwd_strided.argtypes)
+    lib.fa_fwd_strided_noalloc.restype = i32
     lib.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, i32, f32,
                                    ctypes.c_uint64, ctypes.c_uint64, ctypes.POINTER(FaStrides), vp]
     lib.fa_fwd_dropout.restype = i32
@@ -98,6 +100,13 @@ def fa_fwd_strided(Q, K, V, mask, O, L, B, H_q, H_kv, qL, kL, D, scale, causal, 
     ref = ctypes.byref(strides) if strides is not None else None
     return load_library().fa_fwd_strided(Q, K, V, mask, O, L, B, H_q, H_kv, qL, kL, D, scale, causal, dtype,
                                          mask_kind, ref, hip_stream)
+
+
+def fa_fwd_strided_noalloc(Q, K, V, mask, O, L, B, H_q, H_kv, qL, kL, D, scale, causal, dtype, mask_kind, strides,
+                           hip_stream) -> int:
+    ref = ctypes.byref(strides) if strides is not None else None
+    return load_library().fa_fwd_strided_noalloc(Q, K, V, mask, O, L, B, H_q, H_kv, qL, kL, D, scale, causal, dtype,
+                                                 mask_kind, ref, hip_stream)
 
 
 def fa_supported(dtype, D, mask_kind, causal) -> int:
@@ -146,7 +155,7 @@ def _check_extent(t, shape, strides, name):
 
 
 def fwd(q, k, v, *, mask=None, causal=False, scale=None, out=None, lse=None, stream=None, dropout_p=None, seed=0,
-        offset=0, window=None):
+        offset=0, window=None, no_alloc=False):
     """O, L = attention forward on the GPU through libfa_mi355x.
 
     q [B, H_q, qL, D]; k, v [B, H_kv, kL, D]: bf16 or fp32 CUDA tensors whose
@@ -164,6 +173,9 @@ def fwd(q, k, v, *, mask=None, causal=False, scale=None, out=None, lse=None, str
     fp32 at every D).
     window: None, or a causal sliding window of that many keys (row i sees
     keys i - window + 1 .. i; fa_fwd_window, causal only).
+    no_alloc: call fa_fwd_strided_noalloc (no window or dropout): split
+    partials go to the library's static per-GPU scratch; calls that overlap
+    on one GPU must be serialised by the caller.
     """
     import torch
 
@@ -236,7 +248,13 @@ def fwd(q, k, v, *, mask=None, causal=False, scale=None, out=None, lse=None, str
         stream = torch.cuda.current_stream(q.device)
     if window is not None and dropout_p is not None:
         raise ValueError("fa: window and dropout_p are not combined")
-    if window is not None:
+    if no_alloc and (window is not None or dropout_p is not None):
+        raise ValueError("fa: no_alloc has no window or dropout variant")
+    if no_alloc:
+        check(fa_fwd_strided_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, out.data_ptr(), lse.data_ptr(),
+                                     B, Hq, Hkv, qL, kL, D, float(scale), int(bool(causal)), dtype, mask_kind, st,
+                                     stream.cuda_stream))
+    elif window is not None:
         check(fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, out.data_ptr(), lse.data_ptr(),
                             B, Hq, Hkv, qL, kL, D, float(scale), int(bool(causal)), dtype, mask_kind, int(window),
                             st, stream.cuda_stream))

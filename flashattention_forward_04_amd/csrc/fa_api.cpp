@@ -89,6 +89,40 @@ hipError_t library_pool(hipMemPool_t* out)
     return status[dev];
 }
 
+// Scratch of fa_fwd_strided_noalloc: the partials of a split key range.
+// The split plan fills the GPU once, so n_split * (rows of the launch) is at
+// most 256 CUs x 8 resident waves x 32 rows = 65536, and the partials
+// (n_split * rows * (D + 1) fp32) at most 65536 * 257 * 4 bytes at D = 256
+// and 65536 * 129 * 4 bytes at D = 128: under kScratchBytes for every shape
+// (the size is still checked before each launch).  One copy per GPU, in the
+// library's device image, held until the process ends.  Host code never
+// passes `scratch` itself to a kernel (in host code the name is only a
+// stand-in): it uses the device address hipGetSymbolAddress gives for it.
+constexpr size_t kScratchBytes = 36ull << 20;
+static_assert(kScratchBytes == FA_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current.
+hipError_t scratch_address(float** out)
+{
+    constexpr int kMaxDevices = 64;
+    static std::once_flag once[kMaxDevices];
+    static float* ptrs[kMaxDevices];
+    static hipError_t status[kMaxDevices];
+    int dev = 0;
+    const hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(once[dev], [dev]() {
+        void* ptr = nullptr;
+        status[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        ptrs[dev] = (float*)ptr;
+    });
+    *out = ptrs[dev];
+    return status[dev];
+}
+
 }  // namespace fa
 
 namespace {
@@ -203,7 +237,8 @@ fa_status fwd_impl(const void* Q, const void* K, const void* V, const void* mask
                    int B, int H_q, int H_kv, int qL, int kL, int D,
                    float scale, int causal,
                    fa_dtype dtype, fa_mask_kind mask_kind,
-                   const fa_strides* strides, void* hip_stream, const DropArgs* drop, int window = 0)
+                   const fa_strides* strides, void* hip_stream, const DropArgs* drop, int window = 0,
+                   bool noalloc = false)
 {
     g_last_error[0] = '\0';
     const fa_status E = FA_ERR_INVALID_ARGUMENT;
@@ -302,7 +337,24 @@ fa_status fwd_impl(const void* Q, const void* K, const void* V, const void* mask
     }
     if ((int64_t)p.n_qtiles * H_q * B > 0x7fffffffLL) return fail(E, "fa_fwd: grid too large");
 
-    const hipError_t err = var->launch(p, (hipStream_t)hip_stream);
+    if (noalloc) {
+        // the partials of a split launch go to the static scratch, never to
+        // allocated memory; a launch that would need more is refused
+        size_t need = 0;
+        hipError_t perr = var->launch(p, (hipStream_t)hip_stream, &need);
+        if (perr != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd_strided_noalloc: planning of %s failed: %s", var->name,
+                                            hipGetErrorString(perr));
+        if (need > fa::kScratchBytes)
+            return fail(E, "fa_fwd_strided_noalloc: this launch needs %zu bytes of scratch, more than the %zu-byte "
+                        "maximum", need, fa::kScratchBytes);
+        if (need > 0) {
+            perr = fa::scratch_address(&p.ws);
+            if (perr != hipSuccess)
+                return fail(FA_ERR_HIP, "fa_fwd_strided_noalloc: no scratch on this device: %s", hipGetErrorString(perr));
+            p.ws_bytes = fa::kScratchBytes;
+        }
+    }
+    const hipError_t err = var->launch(p, (hipStream_t)hip_stream, nullptr);
     if (err != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd: launch of %s failed: %s", var->name, hipGetErrorString(err));
     return FA_OK;
 }
@@ -320,6 +372,17 @@ fa_status fa_fwd_strided(const void* Q, const void* K, const void* V, const void
 {
     return fwd_impl(Q, K, V, mask, O, L, B, H_q, H_kv, qL, kL, D, scale, causal, dtype, mask_kind, strides,
                     hip_stream, nullptr);
+}
+
+fa_status fa_fwd_strided_noalloc(const void* Q, const void* K, const void* V, const void* mask,
+                                 void* O, float* L,
+                                 int B, int H_q, int H_kv, int qL, int kL, int D,
+                                 float scale, int causal,
+                                 fa_dtype dtype, fa_mask_kind mask_kind,
+                                 const fa_strides* strides, void* hip_stream)
+{
+    return fwd_impl(Q, K, V, mask, O, L, B, H_q, H_kv, qL, kL, D, scale, causal, dtype, mask_kind, strides,
+                    hip_stream, nullptr, 0, true);
 }
 
 fa_status fa_fwd_dropout(const void* Q, const void* K, const void* V, const void* mask,

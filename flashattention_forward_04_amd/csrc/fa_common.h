@@ -52,6 +52,11 @@ struct FwdParams {
     uint32_t drop_thresh;       // ceil(p 2^24) 2^8 (mod 2^32): keep iff the word is >= it
     uint32_t seed_lo, seed_hi;  // the generator's key
     uint32_t off_lo, off_hi;    // 64-bit offset added to every counter
+    // Scratch for the partials of a split launch, given by the caller of the
+    // launcher (fa_fwd_strided_noalloc), ws_bytes long; null: the launcher
+    // takes the partials from the library's pool.
+    float* ws;
+    size_t ws_bytes;
 };
 
 enum MaskKind { MASK_NONE = 0, MASK_ADD = 1, MASK_BOOL = 2 };
@@ -177,7 +182,10 @@ __device__ __forceinline__ void dropout_quad(const FwdParams& p, int64_t n0, flo
 }
 
 // One compiled variant: its launch function and shape facts the host needs.
-typedef hipError_t (*LaunchFn)(const FwdParams&, hipStream_t);
+// With `need` non-null a launch function only plans: it stores the scratch
+// bytes its launch would take for the partials of a split key range (0 for
+// none) and launches nothing.
+typedef hipError_t (*LaunchFn)(const FwdParams&, hipStream_t, size_t* need);
 
 struct Variant {
     const char* name;

@@ -850,7 +850,7 @@ int split_plan(const FwdParams& p, int64_t wgs, int wgs_per_cu_, int* split_tile
 }
 
 template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB, bool DROP = false>
-hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
+hipError_t launch_bf16(const FwdParams& p, hipStream_t st, size_t* need = nullptr)
 {
     // the work-group kernel divides its grid index by n_split
     if (p.n_split < 1) return hipErrorInvalidValue;
@@ -860,21 +860,33 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
                                     : (int64_t)p.n_qtiles * p.Hq * p.B;
     int split_tiles = 0;
     const int n_split = split_plan<CAUSAL, BN, NB>(p, wgs, kWgsPerCu, &split_tiles);
+    const int64_t rows = (int64_t)p.B * p.Hq * p.qL;
+    const size_t ws_bytes = n_split < 2 ? 0 : (size_t)n_split * rows * (D + 1) * sizeof(float);
+    if (need) {
+        *need = ws_bytes;
+        return hipSuccess;
+    }
     if (n_split < 2) {
         q.pair_tiles = CAUSAL && grid_fits_at_once(wgs, kWgsPerCu);
         hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB, DROP>), dim3((unsigned)wgs),
                            dim3(NW * 64), 0, st, q);
         return hipGetLastError();
     }
-    // partials from the library's stream-ordered pool: freed (for reuse by
-    // later calls on this stream) once the merge has read them
-    const int64_t rows = (int64_t)p.B * p.Hq * p.qL;
-    void* ws = nullptr;
-    hipMemPool_t pool;
-    hipError_t err = library_pool(&pool);
-    if (err != hipSuccess) return err;
-    err = hipMallocFromPoolAsync(&ws, (size_t)n_split * rows * (D + 1) * sizeof(float), pool, st);
-    if (err != hipSuccess) return err;
+    // partials in the caller's scratch, or from the library's stream-ordered
+    // pool, freed (for reuse by later calls on this stream) once the merge has
+    // read them.  Every partial the merge reads is written by this launch
+    // first, so the scratch needs no clearing.
+    void* ws = p.ws;
+    hipError_t err = hipSuccess;
+    if (ws != nullptr) {
+        if (p.ws_bytes < ws_bytes) return hipErrorInvalidValue;
+    } else {
+        hipMemPool_t pool;
+        err = library_pool(&pool);
+        if (err != hipSuccess) return err;
+        err = hipMallocFromPoolAsync(&ws, ws_bytes, pool, st);
+        if (err != hipSuccess) return err;
+    }
     q.o_part = (float*)ws;
     q.l_part = q.o_part + (int64_t)n_split * rows * D;
     q.n_split = n_split;
@@ -887,6 +899,7 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t st)
         hipLaunchKernelGGL((merge_splits_bf16_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, q);
         err = hipGetLastError();
     }
+    if (p.ws != nullptr) return err;
     const hipError_t ferr = hipFreeAsync(ws, st);
     return err != hipSuccess ? err : ferr;
 }
@@ -1406,7 +1419,7 @@ constexpr int kShortKeys = 256;
 // Query ranges up to this many rows take 2-wave work-groups.
 constexpr int kShortQueries = 64;
 template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB>
-hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
+hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st, size_t* need = nullptr)
 {
     // (the work-group launcher rejects n_split < 1; the other kernels ignore it)
     if (p.n_split < 1) return hipErrorInvalidValue;
@@ -1421,6 +1434,10 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
             int per_head = (kResident + heads - 1) / heads;
             per_head = max(1, min(per_head, blocks / 4));
             const dim3 grid((unsigned)(per_head * heads));
+            if (need) {
+                *need = 0;
+                return hipSuccess;
+            }
             hipLaunchKernelGGL((fwd_bf16_stream_kernel<D, CAUSAL, 4, 4>), grid, dim3(4 * 64), 0, st, p, per_head);
             return hipGetLastError();
         }
@@ -1438,7 +1455,7 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
             } else {
                 q.n_qtiles = (p.qL + 63) / 64;
             }
-            return launch_bf16<D, MASK, CAUSAL, 2, BN, WPE, SCHED, NB>(q, st);
+            return launch_bf16<D, MASK, CAUSAL, 2, BN, WPE, SCHED, NB>(q, st, need);
         }
     }
     if constexpr (D == 256) {
@@ -1454,6 +1471,10 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
             q.n_qtiles = (p.qL + 31) / 32;
             q.pair_tiles = CAUSAL && grid_fits_at_once((int64_t)q.n_qtiles * q.Hq * q.B, 1);
             const dim3 grid((unsigned)q.n_qtiles * q.Hq * q.B);
+            if (need) {
+                *need = 0;
+                return hipSuccess;
+            }
             hipLaunchKernelGGL((fwd_bf16_split_kernel<D, MASK, CAUSAL, 4, 32>), grid, dim3(4 * 64), 0, st, q);
             return hipGetLastError();
         }
@@ -1466,10 +1487,10 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st)
         if (p.kL <= kShortKeys) {
             FwdParams q = p;
             q.n_qtiles = (p.qL + 127) / 128;
-            return launch_bf16<D, MASK, CAUSAL, 4, 32, 2, 0, 2>(q, st);
+            return launch_bf16<D, MASK, CAUSAL, 4, 32, 2, 0, 2>(q, st, need);
         }
     }
-    return launch_bf16<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB>(p, st);
+    return launch_bf16<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB>(p, st, need);
 }
 
 }  // namespace

@@ -348,8 +348,12 @@ fwd_f32_kernel(const FwdParams p)
 }
 
 template <int D, int MASK, bool CAUSAL, int NW, int BN, bool DROP = false>
-hipError_t launch_f32(const FwdParams& p, hipStream_t st)
+hipError_t launch_f32(const FwdParams& p, hipStream_t st, size_t* need = nullptr)
 {
+    if (need) {
+        *need = 0;  // never splits its key range
+        return hipSuccess;
+    }
     FwdParams q = p;
     const int64_t wgs = (int64_t)p.n_qtiles * p.Hq * p.B;
     q.pair_tiles = CAUSAL && grid_fits_at_once(wgs, 1);

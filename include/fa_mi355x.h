@@ -34,7 +34,8 @@
  *     for itself on each device (hipMemPoolCreate; it keeps up to 256 MiB of
  *     freed memory for reuse).  They are returned to that pool on
  *     `hip_stream` after the merge.  The device's default pool and every
- *     other process-wide allocator setting are left untouched.
+ *     other process-wide allocator setting are left untouched.  Callers that
+ *     cannot allocate use fa_fwd_strided_noalloc.
  *   - All argument checks run before any launch: a failed check writes
  *     nothing, launches nothing and returns FA_ERR_INVALID_ARGUMENT (or
  *     FA_ERR_UNSUPPORTED for a valid combination that is not built), with a
@@ -120,6 +121,32 @@ fa_status fa_fwd_strided(const void* Q, const void* K, const void* V, const void
                          float scale, int causal,
                          fa_dtype dtype, fa_mask_kind mask_kind,
                          const fa_strides* strides, void* hip_stream);
+
+/*
+ * fa_fwd_strided_noalloc - fa_fwd_strided for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same arguments, checks and results: the
+ * same kernels and split plan run, so O and L are bitwise those of
+ * fa_fwd_strided.  The fp32 partials of a split key range go to a static
+ * scratch array of FA_NOALLOC_SCRATCH_BYTES in the library's device image,
+ * one per GPU, held until the process ends.  The split plan never needs more
+ * than 65536 * (D + 1) * 4 bytes (33.8 MB at D = 128), so every shape fits;
+ * a call that would need more returns FA_ERR_INVALID_ARGUMENT before
+ * launching anything.  The first call on a device looks the array up there
+ * (hipGetSymbolAddress); no call allocates or calls an allocating routine.
+ * Every call on a GPU shares that GPU's scratch and leaves its partials
+ * there: calls that overlap on one GPU (on different streams or from
+ * different host threads) race, and the caller must serialise them.  Nothing
+ * in the scratch needs to start at zero: a launch writes every partial it
+ * reads.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (36u << 20)
+fa_status fa_fwd_strided_noalloc(const void* Q, const void* K, const void* V, const void* mask,
+                                 void* O, float* L,
+                                 int B, int H_q, int H_kv, int qL, int kL, int D,
+                                 float scale, int causal,
+                                 fa_dtype dtype, fa_mask_kind mask_kind,
+                                 const fa_strides* strides, void* hip_stream);
 
 /*
  * fa_fwd_strided with dropout on the attention weights (ruDNN
