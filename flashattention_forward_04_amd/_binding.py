@@ -18,8 +18,9 @@ FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_DTYPE_F32, FA_DTYPE_BF16 = 0, 1
 FA_MASK_NONE, FA_MASK_ADDITIVE, FA_MASK_BOOL = 0, 1, 2
 
-EXPORTS = ("fa_fwd", "fa_fwd_strided", "fa_fwd_strided_noalloc", "fa_fwd_dropout", "fa_fwd_window", "fa_supported",
-           "fa_variant_count", "fa_variant_name", "fa_status_string", "fa_last_error", "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_strided", "fa_fwd_strided_noalloc", "fa_fwd_dropout", "fa_fwd_window", "fa_bwd",
+           "fa_supported", "fa_bwd_supported", "fa_variant_count", "fa_variant_name", "fa_status_string",
+           "fa_last_error", "fa_abi_version")
 
 
 class FaError(RuntimeError):
@@ -61,8 +62,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, i32, i32,
                                   ctypes.POINTER(FaStrides), vp]
     lib.fa_fwd_window.restype = i32
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32,
+                           i32, vp]
+    lib.fa_bwd.restype = i32
     lib.fa_supported.argtypes = [i32, i32, i32, i32]
     lib.fa_supported.restype = i32
+    lib.fa_bwd_supported.argtypes = [i32, i32, i32, i32]
+    lib.fa_bwd_supported.restype = i32
     lib.fa_variant_count.restype = i32
     lib.fa_variant_name.argtypes = [i32]
     lib.fa_variant_name.restype = ctypes.c_char_p
@@ -109,8 +115,18 @@ def fa_fwd_strided_noalloc(Q, K, V, mask, O, L, B, H_q, H_kv, qL, kL, D, scale, 
                                                  mask_kind, ref, hip_stream)
 
 
+def fa_bwd(Q, K, V, O, dO, L, mask, Delta, dQ, dK, dV, B, H_q, H_kv, qL, kL, D, scale, causal, dtype, mask_kind,
+           hip_stream) -> int:
+    return load_library().fa_bwd(Q, K, V, O, dO, L, mask, Delta, dQ, dK, dV, B, H_q, H_kv, qL, kL, D, scale, causal,
+                                 dtype, mask_kind, hip_stream)
+
+
 def fa_supported(dtype, D, mask_kind, causal) -> int:
     return load_library().fa_supported(dtype, D, mask_kind, causal)
+
+
+def fa_bwd_supported(dtype, D, mask_kind, causal) -> int:
+    return load_library().fa_bwd_supported(dtype, D, mask_kind, causal)
 
 
 def fa_variant_count() -> int:
@@ -268,3 +284,54 @@ def fwd(q, k, v, *, mask=None, causal=False, scale=None, out=None, lse=None, str
                              float(dropout_p), int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1), st,
                              stream.cuda_stream))
     return out, lse
+
+
+def bwd(q, k, v, o, do, lse, *, mask=None, causal=False, scale=None, dq=None, dk=None, dv=None, delta=None,
+        stream=None):
+    """dQ, dK, dV (and Delta = rowsum(dO * O)) of the attention forward pass
+    on the GPU through libfa_mi355x (fa_bwd).
+
+    q, o, do [B, H_q, qL, D] and k, v [B, H_kv, kL, D]: contiguous bf16 CUDA
+    tensors; o and lse are fwd's outputs for the same q, k, v, mask, scale
+    and causal.  mask: None, bool/uint8 (nonzero = attend) or additive of q's
+    dtype, contiguous [B, H_q, qL, kL].  Returns (dq, dk, dv, delta).
+    """
+    import torch
+
+    B, Hq, qL, D = q.shape
+    Bk, Hkv, kL, Dk = k.shape
+    for t, n, shape in ((q, "q", (B, Hq, qL, D)), (o, "o", (B, Hq, qL, D)), (do, "do", (B, Hq, qL, D)),
+                        (k, "k", (B, Hkv, kL, D)), (v, "v", (B, Hkv, kL, D))):
+        if not t.is_cuda or t.dtype != q.dtype or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"fa.bwd: {n} must be a contiguous CUDA tensor of shape {shape} and q's dtype")
+    if tuple(lse.shape) != (B, Hq, qL) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("fa.bwd: lse must be a contiguous fp32 [B, H_q, qL] tensor")
+    dtype = FA_DTYPE_BF16 if q.dtype == torch.bfloat16 else FA_DTYPE_F32
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    delta = torch.empty_like(lse) if delta is None else delta
+    for t, ref, n in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv"), (delta, lse, "delta")):
+        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous():
+            raise ValueError(f"fa.bwd: {n} must be contiguous, shaped and typed like {'lse' if n == 'delta' else n[1:]}")
+    mask_kind, mptr = FA_MASK_NONE, None
+    if mask is not None:
+        if mask.dtype in (torch.bool, torch.uint8):
+            mask_kind = FA_MASK_BOOL
+            if mask.dtype == torch.bool:
+                mask = mask.view(torch.uint8)
+        elif mask.dtype == q.dtype:
+            mask_kind = FA_MASK_ADDITIVE
+        else:
+            raise ValueError("fa.bwd: an additive mask must have q's dtype; a bool mask must be bool or uint8")
+        if tuple(mask.shape) != (B, Hq, qL, kL) or not mask.is_contiguous() or not mask.is_cuda:
+            raise ValueError("fa.bwd: mask must be a contiguous CUDA [B, H_q, qL, kL] tensor")
+        mptr = mask.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    check(fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), mptr,
+                 delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, qL, kL, D, float(scale),
+                 int(bool(causal)), dtype, mask_kind, stream.cuda_stream))
+    return dq, dk, dv, delta

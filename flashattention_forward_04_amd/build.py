@@ -21,10 +21,12 @@ LIB = os.path.join(PKG, "libfa_mi355x.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
-# One translation unit per (dtype, head dim), so the library compiles in
-# parallel, plus the C ABI.
+# One translation unit per (pass, dtype, head dim), so the library compiles
+# in parallel, plus the C ABI.
 HEAD_DIMS = (16, 32, 48, 64, 80, 96, 128, 256)
-SOURCES = ["fa_api.cpp", *[f"fa_fwd_bf16_d{d}.hip" for d in HEAD_DIMS], *[f"fa_fwd_f32_d{d}.hip" for d in HEAD_DIMS]]
+BWD_HEAD_DIMS = (64, 128)
+SOURCES = ["fa_api.cpp", *[f"fa_fwd_bf16_d{d}.hip" for d in HEAD_DIMS], *[f"fa_fwd_f32_d{d}.hip" for d in HEAD_DIMS],
+           *[f"fa_bwd_bf16_d{d}.hip" for d in BWD_HEAD_DIMS]]
 
 # Per-source code generation options.  The bf16 kernels keep every matrix
 # accumulator in ordinary VGPRs: their softmax works on the score

@@ -8,6 +8,7 @@
 // and stride rules.  Everything is checked before anything is launched.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -56,6 +57,22 @@ FA_TABLE_OF(f32)
 FA_TABLE_OF(bf16_dropout)
 FA_TABLE_OF(f32_dropout)
 #undef FA_TABLE_OF
+
+const BwdVariant* bwd_variants_bf16(int* n)
+{
+    static std::vector<BwdVariant> all;
+    static std::once_flag once;
+    std::call_once(once, []() {
+        const BwdVariant* (*fns[])(int*) = {bwd_variants_bf16_d64, bwd_variants_bf16_d128};
+        for (auto fn : fns) {
+            int k = 0;
+            const BwdVariant* t = fn(&k);
+            all.insert(all.end(), t, t + k);
+        }
+    });
+    *n = (int)all.size();
+    return all.data();
+}
 
 // Partials of split launches come from a stream-ordered memory pool that the
 // library creates for itself, one per device.  The process-wide default pool
@@ -206,7 +223,9 @@ int fa_variant_count(void)
         variant_table(w, &n);
         total += n;
     }
-    return total;
+    int nb = 0;
+    fa::bwd_variants_bf16(&nb);
+    return total + nb;
 }
 
 const char* fa_variant_name(int i)
@@ -218,7 +237,24 @@ const char* fa_variant_name(int i)
         if (i < n) return t[i].name;
         i -= n;
     }
+    int nb = 0;
+    const fa::BwdVariant* tb = fa::bwd_variants_bf16(&nb);
+    return i < nb ? tb[i].name : nullptr;
+}
+
+static const fa::BwdVariant* find_bwd_variant(int dtype, int D, int mask, int causal)
+{
+    if (dtype != FA_DTYPE_BF16) return nullptr;
+    int n = 0;
+    const fa::BwdVariant* t = fa::bwd_variants_bf16(&n);
+    for (int i = 0; i < n; ++i)
+        if (t[i].D == D && t[i].mask == mask && t[i].causal == (causal ? 1 : 0)) return &t[i];
     return nullptr;
+}
+
+int fa_bwd_supported(fa_dtype dtype, int D, fa_mask_kind mask_kind, int causal)
+{
+    return find_bwd_variant(dtype, D, mask_kind, causal) != nullptr;
 }
 
 int fa_supported(fa_dtype dtype, int D, fa_mask_kind mask_kind, int causal)
@@ -411,6 +447,73 @@ fa_status fa_fwd_window(const void* Q, const void* K, const void* V, const void*
     }
     return fwd_impl(Q, K, V, mask, O, L, B, H_q, H_kv, qL, kL, D, scale, causal, dtype, mask_kind, strides,
                     hip_stream, nullptr, window);
+}
+
+fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L,
+                 const void* mask, float* Delta, void* dQ, void* dK, void* dV,
+                 int B, int H_q, int H_kv, int qL, int kL, int D,
+                 float scale, int causal,
+                 fa_dtype dtype, fa_mask_kind mask_kind, void* hip_stream)
+{
+    g_last_error[0] = '\0';
+    const fa_status E = FA_ERR_INVALID_ARGUMENT;
+    if (B <= 0) return fail(E, "fa_bwd: B must be > 0, got %d", B);
+    if (H_q <= 0) return fail(E, "fa_bwd: H_q must be > 0, got %d", H_q);
+    if (H_kv <= 0) return fail(E, "fa_bwd: H_kv must be > 0, got %d", H_kv);
+    if (H_q % H_kv != 0) return fail(E, "fa_bwd: H_q (%d) must be divisible by H_kv (%d)", H_q, H_kv);
+    if (qL <= 0) return fail(E, "fa_bwd: qL must be > 0, got %d", qL);
+    if (kL <= 0) return fail(E, "fa_bwd: kL must be > 0, got %d", kL);
+    if (D != 16 && D != 32 && D != 48 && D != 64 && D != 80 && D != 96 && D != 128 && D != 256)
+        return fail(E, "fa_bwd: D must be 16, 32, 48, 64, 80, 96, 128 or 256, got %d", D);
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return fail(E, "fa_bwd: unknown dtype %d", (int)dtype);
+    if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_ADDITIVE && mask_kind != FA_MASK_BOOL)
+        return fail(E, "fa_bwd: unknown mask kind %d", (int)mask_kind);
+    if ((mask_kind == FA_MASK_NONE) != (mask == nullptr))
+        return fail(E, "fa_bwd: mask must be NULL exactly when mask_kind is FA_MASK_NONE");
+    if (!Q || !K || !V || !O || !dO || !L || !Delta || !dQ || !dK || !dV)
+        return fail(E, "fa_bwd: Q, K, V, O, dO, L, Delta, dQ, dK and dV must be non-NULL");
+    if (!std::isfinite(scale)) return fail(E, "fa_bwd: scale must be finite");
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(dO, 16) ||
+        !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16) || !aligned(L, 4) || !aligned(Delta, 4))
+        return fail(E, "fa_bwd: Q, K, V, O, dO, dQ, dK and dV must be 16-byte aligned, L and Delta 4-byte aligned");
+    if ((int64_t)B * H_q * qL * D > INT64_MAX / 8 || (int64_t)B * H_q * qL * kL > INT64_MAX / 8)
+        return fail(E, "fa_bwd: tensor too large");
+    const fa::BwdVariant* var = find_bwd_variant(dtype, D, mask_kind, causal);
+    if (!var)
+        return fail(FA_ERR_UNSUPPORTED, "fa_bwd: no backward kernel built for dtype %d, D %d, mask %d, causal %d "
+                    "(built: bf16, D 64 and 128)", (int)dtype, D, (int)mask_kind, causal);
+    fa::BwdParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.q = Q;
+    p.k = K;
+    p.v = V;
+    p.o = O;
+    p.dout = dO;
+    p.lse = L;
+    p.mask = mask;
+    p.delta = Delta;
+    p.dq = dQ;
+    p.dk = dK;
+    p.dv = dV;
+    default_strides(p.m_s, H_q, qL, kL);
+    p.B = B;
+    p.Hq = H_q;
+    p.Hkv = H_kv;
+    p.qL = qL;
+    p.kL = kL;
+    p.group = H_q / H_kv;
+    p.scale = scale;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    if (mask_kind != FA_MASK_NONE) {
+        const int mesz = mask_kind == FA_MASK_BOOL ? 1 : 2;
+        p.mask_vec = aligned(mask, (uintptr_t)4 * mesz) && kL % 4 == 0;
+    }
+    const int64_t grid = std::max<int64_t>((int64_t)(qL + 127) / 128 * H_q * B, (int64_t)(kL + 127) / 128 * H_kv * B);
+    if (grid > 0x7fffffffLL || (int64_t)B * H_q * qL * (D / 8) / 256 > 0x7fffffffLL)
+        return fail(E, "fa_bwd: grid too large");
+    const hipError_t err = var->launch(p, (hipStream_t)hip_stream);
+    if (err != hipSuccess) return fail(FA_ERR_HIP, "fa_bwd: launch of %s failed: %s", var->name, hipGetErrorString(err));
+    return FA_OK;
 }
 
 fa_status fa_fwd(const void* Q, const void* K, const void* V, const void* mask,

@@ -61,6 +61,29 @@ struct FwdParams {
 
 enum MaskKind { MASK_NONE = 0, MASK_ADD = 1, MASK_BOOL = 2 };
 
+// Everything a backward launch needs.  Tensors are contiguous head-major:
+// Q, O, dO, dQ [B, H_q, qL, D]; K, V, dK, dV [B, H_kv, kL, D]; L and Delta
+// [B, H_q, qL] fp32.
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    const float* lse;   // natural-log logsumexp of the forward pass
+    const void* mask;
+    float* delta;       // written: rowsum(dO * O)
+    void* dq;
+    void* dk;
+    void* dv;
+    int64_t m_s[3];     // mask strides {batch, head, seq} in elements
+    int B, Hq, Hkv, qL, kL;
+    int group;          // Hq / Hkv
+    float scale;        // natural-domain score scale (signed)
+    float scale_log2;   // scale * log2(e)
+    int mask_vec;       // mask rows admit 4-element vector loads
+};
+
 // Work-groups are dispatched round-robin over the 8 XCDs (each with its own
 // L2): work-group i runs on XCD i % 8.  Within the H_q consecutive
 // work-groups of one (query tile, batch), slot i gets query head
@@ -208,6 +231,21 @@ struct Variant {
     const Variant* variants_f32_dropout_d##D(int* n);
 FA_FOR_EACH_HEAD_DIM(FA_DECLARE_TABLES)
 #undef FA_DECLARE_TABLES
+
+// Backward variants (fa_bwd_bf16_d<D>.hip), host only.
+typedef hipError_t (*BwdLaunchFn)(const BwdParams&, hipStream_t);
+struct BwdVariant {
+    const char* name;
+    int D;
+    int mask;    // MaskKind
+    int causal;
+    BwdLaunchFn launch;
+};
+#define FA_FOR_EACH_BWD_HEAD_DIM(X) X(64) X(128)
+#define FA_DECLARE_BWD_TABLES(D) const BwdVariant* bwd_variants_bf16_d##D(int* n);
+FA_FOR_EACH_BWD_HEAD_DIM(FA_DECLARE_BWD_TABLES)
+#undef FA_DECLARE_BWD_TABLES
+const BwdVariant* bwd_variants_bf16(int* n);
 
 // Every variant of one kind, over all head dims (fa_api.cpp, host only).
 const Variant* variants_bf16(int* n);

@@ -1,6 +1,6 @@
 /*
- * fa_mi355x.h - C ABI of libfa_mi355x, a FlashAttention-2 forward pass for
- * AMD Instinct MI355X (gfx950).
+ * fa_mi355x.h - C ABI of libfa_mi355x, a FlashAttention-2 forward pass (and
+ * its backward pass) for AMD Instinct MI355X (gfx950).
  *
  * The operation (mlx-native flash_attn_train.rs, module doc "Algorithm" and
  * "Buffer layout"; oxibonsai dit_attention_flash.rs, module doc "Flash-attention
@@ -194,13 +194,54 @@ fa_status fa_fwd_window(const void* Q, const void* K, const void* V, const void*
                         fa_dtype dtype, fa_mask_kind mask_kind,
                         int window, const fa_strides* strides, void* hip_stream);
 
+/*
+ * fa_bwd - the backward pass: gradients dQ, dK, dV of the forward output O
+ * for an upstream gradient dO (forge flash_attention_mma.metal, the backward
+ * section's header and its dq / dv / dk kernels; mlx-native
+ * flash_attn_train.rs, "Phase 2 -- FA-2 backward kernel": compute D, then
+ * the backward kernel; ruDNN dense_attention.rs, `backward_kv_owned`).  With
+ * P_ij = exp(s_ij - L_i) the forward pass's softmax weights (0 for keys that
+ * are not allowed; same rules as fa_fwd):
+ *
+ *     Delta_i = sum_d dO[i,d] O[i,d]          (written to Delta)
+ *     dS_ij   = P_ij (dO_i . V_j - Delta_i)
+ *     dQ_i    = scale sum_j dS_ij K_j
+ *     dK_j    = scale sum over the query heads of j's kv head and rows i of dS_ij Q_i
+ *     dV_j    = sum over the query heads of j's kv head and rows i of P_ij dO_i
+ *
+ *   Q, O, dO [B, H_q,  qL, D]  dtype   (read; O and L are fa_fwd's outputs
+ *   K, V     [B, H_kv, kL, D]  dtype    for the same Q, K, V, mask, scale
+ *   L        [B, H_q,  qL]     fp32     and causal)
+ *   mask     [B, H_q,  qL, kL] as fa_fwd (read; NULL iff FA_MASK_NONE); no
+ *            gradient is formed for it
+ *   Delta    [B, H_q,  qL]     fp32    (written: a caller-owned workspace that
+ *                                       holds rowsum(dO * O) on return)
+ *   dQ       [B, H_q,  qL, D]  dtype   (written)
+ *   dK, dV   [B, H_kv, kL, D]  dtype   (written)
+ * All tensors are contiguous head-major.  Built for bf16 at D = 64 and 128,
+ * every mask kind, causal or not; other valid combinations return
+ * FA_ERR_UNSUPPORTED.  Three launches on `hip_stream` (Delta, then dQ, then
+ * dK and dV); no atomics, so the result is deterministic; nothing is
+ * allocated.  Checks as fa_fwd, plus dO, Delta, dQ, dK, dV non-NULL and
+ * aligned (16 bytes; 4 for L and Delta).
+ */
+fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L,
+                 const void* mask, float* Delta, void* dQ, void* dK, void* dV,
+                 int B, int H_q, int H_kv, int qL, int kL, int D,
+                 float scale, int causal,
+                 fa_dtype dtype, fa_mask_kind mask_kind, void* hip_stream);
+
 /* 1 if (dtype, D, mask_kind, causal) has a compiled kernel, else 0. */
 int fa_supported(fa_dtype dtype, int D, fa_mask_kind mask_kind, int causal);
 
+/* 1 if fa_bwd has a compiled kernel for (dtype, D, mask_kind, causal), else 0. */
+int fa_bwd_supported(fa_dtype dtype, int D, fa_mask_kind mask_kind, int causal);
+
 /* Number of compiled kernel variants -- every (dtype, D, mask kind, causal)
- * of fa_fwd, then of fa_fwd_dropout -- and the name of variant i (NULL past
- * the end); the names are static strings (cf. the kernel-name lists that
- * mlx-native flash_attn_train.rs exposes to its tests). */
+ * of fa_fwd, then of fa_fwd_dropout, then of fa_bwd -- and the name of
+ * variant i (NULL past the end); the names are static strings (cf. the
+ * kernel-name lists that mlx-native flash_attn_train.rs exposes to its
+ * tests). */
 int fa_variant_count(void);
 const char* fa_variant_name(int i);
 

@@ -50,10 +50,20 @@ def test_version_and_status_strings(lib):
 
 def test_variant_table_covers_every_combination(lib):
     names = [fa.fa_variant_name(i) for i in range(fa.fa_variant_count())]
-    # every (dtype, D, mask kind, causal) for fa_fwd and again for fa_fwd_dropout
-    assert None not in names and len(set(names)) == len(names) == 192
-    dropout = [n for n in names if n.endswith("_dropout")]
-    assert len(dropout) == 96 and {n[:-len("_dropout")] for n in dropout} == set(names) - set(dropout)
+    # every (dtype, D, mask kind, causal) for fa_fwd and again for fa_fwd_dropout, then the bf16 backward
+    # variants at D = 64 and 128
+    assert None not in names and len(set(names)) == len(names) == 192 + 12
+    bwd = [n for n in names if n.startswith("bwd_")]
+    fwd = [n for n in names if not n.startswith("bwd_")]
+    dropout = [n for n in fwd if n.endswith("_dropout")]
+    assert len(dropout) == 96 and {n[:-len("_dropout")] for n in dropout} == set(fwd) - set(dropout)
+    assert len(bwd) == 12 and {n.replace("bwd_", "fwd_") for n in bwd} <= set(fwd)
+    for D in (64, 128):
+        for mk in (fa.FA_MASK_NONE, fa.FA_MASK_ADDITIVE, fa.FA_MASK_BOOL):
+            for c in (0, 1):
+                assert fa.fa_bwd_supported(fa.FA_DTYPE_BF16, D, mk, c) == 1
+                assert fa.fa_bwd_supported(fa.FA_DTYPE_F32, D, mk, c) == 0
+    assert fa.fa_bwd_supported(fa.FA_DTYPE_BF16, 256, fa.FA_MASK_NONE, 0) == 0
     assert fa.fa_variant_name(len(names)) is None and fa.fa_variant_name(-1) is None
     for dt in (fa.FA_DTYPE_F32, fa.FA_DTYPE_BF16):
         for D in (16, 32, 48, 64, 80, 96, 128, 256):
@@ -183,3 +193,33 @@ def test_window_needs_causal(lib):
 def test_window_checks_the_plain_arguments_too(lib):
     assert _window_call(16, H_q=3) == fa.FA_ERR_INVALID_ARGUMENT
     assert "divisible" in fa.fa_last_error()
+
+
+BWD_BASE = dict(Q=P, K=P, V=P, O=P, dO=P, L=P, mask=None, Delta=P, dQ=P, dK=P, dV=P, B=1, H_q=4, H_kv=2, qL=16,
+                kL=16, D=64, scale=0.125, causal=0, dtype=fa.FA_DTYPE_BF16, mask_kind=fa.FA_MASK_NONE, hip_stream=None)
+
+BWD_BAD = [
+    (dict(B=0), fa.FA_ERR_INVALID_ARGUMENT, "B must be > 0"),
+    (dict(H_q=3), fa.FA_ERR_INVALID_ARGUMENT, "divisible"),
+    (dict(kL=0), fa.FA_ERR_INVALID_ARGUMENT, "kL must be > 0"),
+    (dict(D=72), fa.FA_ERR_INVALID_ARGUMENT, "D must be"),
+    (dict(dtype=9), fa.FA_ERR_INVALID_ARGUMENT, "unknown dtype"),
+    (dict(mask=P), fa.FA_ERR_INVALID_ARGUMENT, "mask must be NULL exactly"),
+    (dict(dO=None), fa.FA_ERR_INVALID_ARGUMENT, "non-NULL"),
+    (dict(Delta=None), fa.FA_ERR_INVALID_ARGUMENT, "non-NULL"),
+    (dict(dK=P + 8), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(Delta=P + 2), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARGUMENT, "finite"),
+    (dict(dtype=fa.FA_DTYPE_F32), fa.FA_ERR_UNSUPPORTED, "no backward kernel"),
+    (dict(D=256), fa.FA_ERR_UNSUPPORTED, "no backward kernel"),
+]
+
+
+@pytest.mark.parametrize("over,status,msg", BWD_BAD, ids=[m + str(i) for i, (_, _, m) in enumerate(BWD_BAD)])
+def test_bwd_rejects_bad_arguments(lib, over, status, msg):
+    a = dict(BWD_BASE, **over)
+    st = fa.fa_bwd(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["L"], a["mask"], a["Delta"], a["dQ"], a["dK"], a["dV"],
+                   a["B"], a["H_q"], a["H_kv"], a["qL"], a["kL"], a["D"], a["scale"], a["causal"], a["dtype"],
+                   a["mask_kind"], a["hip_stream"])
+    assert st == status
+    assert msg in fa.fa_last_error()
