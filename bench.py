@@ -42,16 +42,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the kernel sources: a recorded traffic figure is only
-    reported while the kernels it was measured on are unchanged."""
+def kernel_sources(w) -> list:
+    """The source files the kernels of workload w are compiled from (and the
+    host code that chooses and launches them)."""
+    common = ["fa_common.h", "fa_api.cpp"]
+    if w.backward:
+        return common + ["fa_bwd_bf16.h", f"fa_bwd_bf16_d{w.D}.hip"]
+    kind = "bf16" if w.dtype == "bf16" else "f32"
+    return common + [f"fa_fwd_{kind}.h", f"fa_fwd_{kind}_d{w.D}.hip"]
+
+
+def kernel_source_hash(w) -> str:
+    """sha256 over the sources of w's kernels: a recorded traffic figure is
+    only reported while the kernels it was measured on are unchanged."""
     import hashlib
 
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in sorted(kernel_sources(w)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
@@ -62,7 +71,7 @@ def recorded_traffic(w):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha256") != kernel_source_hash():
+    if rec.get("source_sha256") != kernel_source_hash(w):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -105,7 +114,7 @@ def profile_commands(prof_dir, w):
     return {
         "copy_mib": 1024,
         "trace": f"rocprofv3 --kernel-trace --stats --output-format csv -d {prof_dir}/trace -o trace -- "
-                 f"python3 bench.py {DRIVER_PROTOCOL}{base}",
+                 f"python3 bench.py {DRIVER_PROTOCOL} --no-cpu-baseline{base}",
         "steady": f"rocprofv3 --kernel-trace --stats --output-format csv -d {prof_dir}/steady -o steady -- "
                   f"python3 bench.py {STEADY_PROTOCOL} --no-cpu-baseline{base}",
         "counters": f"rocprofv3 --pmc {counters} --output-format csv -d {prof_dir}/counters -o counters -- "
@@ -167,7 +176,9 @@ def summarize(prof_dir, w, commands):
 
     def trace_summary(sub, steps):
         stats = list(csv.DictReader(open(one(f"{sub}/*kernel_stats.csv"))))
-        rows = [r for r in stats if "fa::" in r["Name"]]
+        # the timed call's kernels: the backward workloads also run the
+        # forward pass once, untimed, to produce O and L
+        rows = [r for r in stats if "fa::" in r["Name"] and (("::bwd_" in r["Name"]) == bool(w.backward))]
         if not rows:
             raise RuntimeError(f"no fa:: kernel in the {sub} kernel-trace stats")
         # one call may launch more than one kernel (a split key range: the
@@ -278,7 +289,7 @@ def summarize(prof_dir, w, commands):
            "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
            "hbm_bytes_per_launch": fetch + write, "algorithmic_bytes": alg,
            "fetch_scale": f_factor, "write_scale": w_factor, "counters": ctr_rec,
-           "source_sha256": kernel_source_hash()}
+           "source_sha256": kernel_source_hash(w), "sources": sorted(kernel_sources(w))}
     with open(os.path.join(PROFILES, f"{w.name}.traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
     first = per_kernel[0][3]
@@ -343,7 +354,8 @@ def summarize(prof_dir, w, commands):
         f"(roofline bound: {roofline_bound(w)}"
         + (f"; {buffer_sets(w)} buffer sets rotated" if roofline_bound(w) == "hbm" else "") + ").",
         "",
-        f"Kernel source sha256 {rec['source_sha256'][:16]}...; bench.py reports this traffic only while it matches.",
+        f"Kernel source sha256 {rec['source_sha256'][:16]}... over {', '.join(rec['sources'])}; bench.py reports "
+        "this traffic only while it matches.",
         "",
     ]
     with open(os.path.join(PROFILES, f"{w.name}.md"), "w") as f:
@@ -353,7 +365,7 @@ def summarize(prof_dir, w, commands):
 
 def find_workload(W, name):
     every = {x.name: x for x in (*W.CONFIGS.values(), *W.SHORT_KL, *W.HEAD_DIMS, *W.SPLIT_KV, *W.DROPOUT,
-                                 *W.WINDOW, *W.RAGGED)}
+                                 *W.WINDOW, *W.RAGGED, *W.BACKWARD)}
     if name not in every:
         raise SystemExit(f"unknown workload {name!r}; known: {', '.join(sorted(every))}")
     return every[name]
@@ -373,9 +385,11 @@ def buffer_sets(w) -> int:
 
 
 def algorithmic_bytes(w) -> int:
+    """Bytes every launch must move at least once: Q, K, V, O, L (and the
+    mask); the backward pass reads Q, K, V, O, dO, L and writes dQ, dK, dV."""
     esz = 2 if w.dtype == "bf16" else 4
-    qo = 2 * w.B * w.Hq * w.qL * w.D * esz
-    kv = 2 * w.B * w.Hkv * w.kL * w.D * esz
+    qo = (5 if w.backward else 2) * w.B * w.Hq * w.qL * w.D * esz
+    kv = (4 if w.backward else 2) * w.B * w.Hkv * w.kL * w.D * esz
     lse = w.B * w.Hq * w.qL * 4
     mask = 0
     if w.mask_kind == "additive":
@@ -495,8 +509,23 @@ def main():
     if n_sets > 1:
         log(f"rotating {n_sets} buffer sets, {n_sets * algorithmic_bytes(w) / 1e6:.0f} MB of inputs and outputs")
 
+    if w.backward:
+        # the forward pass once (its O and L feed every backward step), then
+        # the gradient buffers; a step is one fa_bwd call
+        dod = W.draw_grad(w).to(dev)
+        grads = []
+        for qd, kd, vd, md, out, lse in sets:
+            fa.fwd(qd, kd, vd, mask=md, causal=w.causal, scale=w.scale, out=out, lse=lse, stream=stream)
+            grads.append((torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd), torch.empty_like(lse)))
+        torch.cuda.synchronize()
+
     def step(i):
         qd, kd, vd, md, out, lse = sets[i % n_sets]
+        if w.backward:
+            dq, dk, dv, delta = grads[i % n_sets]
+            fa.bwd(qd, kd, vd, out, dod, lse, mask=md, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv,
+                   delta=delta, stream=stream)
+            return
         fa.fwd(qd, kd, vd, mask=md, causal=w.causal, scale=w.scale, out=out, lse=lse, stream=stream,
                dropout_p=w.dropout_p, seed=w.seed, window=w.window)
 
@@ -537,7 +566,7 @@ def main():
         f"({100 * nbytes / (kern_avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS:.1f}% of HBM)")
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not w.backward:
         cpu = cpu_baseline(w, q, k, v, mask, args.cpu_seconds)
         log(f"cpu baseline: {cpu}")
 
@@ -568,6 +597,7 @@ def main():
                    "causal": w.causal, "mask": w.mask_kind, "scale": w.scale,
                    **({"dropout": w.dropout_p} if w.dropout_p is not None else {}),
                    **({"window": w.window} if w.window is not None else {}),
+                   **({"pass": "backward"} if w.backward else {}),
                    "o_layout": "token-major" if w.token_major_out else "head-major",
                    "flop_per_step": flops},
         "mfma_peak_frac": round(achieved / peak, 4),

@@ -41,11 +41,16 @@ class Workload:
     seed: int = 0
     dropout_p: float | None = None  # dropout rate on the attention weights (seed = the workload seed)
     window: int | None = None       # causal sliding window: row i sees keys i - window + 1 .. i
+    backward: bool = False          # time fa_bwd (dQ, dK, dV) instead of the forward pass
     note: str = ""
 
     def flops(self) -> float:
         """Algorithmic FLOP: 4*B*Hq*qL*kL*D, halved when causal; with a window,
-        4*B*Hq*D times the exact count of allowed (row, key) pairs."""
+        4*B*Hq*D times the exact count of allowed (row, key) pairs.  The
+        backward pass counts its five matrix products (S, dP, dV, dK, dQ):
+        2.5 times the forward figure."""
+        if self.backward:
+            return 2.5 * self.with_(backward=False).flops()
         if self.window is not None:
             i = np.arange(self.qL, dtype=np.int64)
             pairs = np.minimum(np.minimum(i + 1, self.window), np.maximum(0, self.kL - np.maximum(0, i - self.window + 1)))
@@ -113,6 +118,13 @@ WINDOW = [
              seed=80, window=4096, note="long-context causal bf16 under a 4096-key sliding window"),
 ]
 
+# The backward pass (dQ, dK, dV) at the causal GQA training shape and the
+# long-context shape; dO ~ N(0, 1) drawn by draw_grad.
+BACKWARD = [
+    C2.with_(name="bwd_causal_gqa_bf16_d64", backward=True, note="backward pass, causal GQA bf16 training shape"),
+    C3.with_(name="bwd_causal_bf16_d128_8k", backward=True, note="backward pass, long-context causal bf16 D=128"),
+]
+
 # Ragged shapes that are not tile multiples (the configs above all are).
 RAGGED = [
     Workload("ragged_masked_d256", "bf16", 1, 2, 2, 1000, 3000, 256, 1 / 16, mask_kind="additive",
@@ -173,3 +185,10 @@ def sample_rows(w: Workload, n: int, seed: int = 1234) -> np.ndarray:
     extra = rng.integers(0, w.B * w.Hq * w.qL, size=max(0, n - len(rows)))
     rows.update(int(x) for x in extra)
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def draw_grad(w: Workload):
+    """The upstream gradient dO ~ N(0, 1) [B, Hq, qL, D] in the workload dtype
+    (its own generator, seeded from the workload seed)."""
+    rng = np.random.default_rng(w.seed + 1000)
+    return torch.from_numpy(rng.standard_normal((w.B, w.Hq, w.qL, w.D), dtype=np.float32)).to(w.torch_dtype())
