@@ -76,6 +76,10 @@ fwd_f32_kernel(const FwdParams p)
     int id = blockIdx.x;
     const int h = head_of(id % p.Hq, p.Hq);
     id /= p.Hq;
+    // key range split over work-groups (n_split > 1): this work-group takes
+    // key tiles [split * split_tiles, (split + 1) * split_tiles)
+    const int split = id % p.n_split;
+    id /= p.n_split;
     const int b = id % p.B;
     id /= p.B;
     const int qt = CAUSAL ? causal_tile(id, p.n_qtiles, p.pair_tiles) : id;
@@ -106,7 +110,7 @@ fwd_f32_kernel(const FwdParams p)
     // causal sliding window: rows see keys from i - window + 1 on, so the
     // work-group starts at the tile of its first row's first key
     const bool win = CAUSAL && p.window > 0;
-    const int t_first = win ? max(0, q0 - p.window + 1) / BN : 0;
+    const int t_first = (win ? max(0, q0 - p.window + 1) / BN : 0) + split * p.split_tiles;
 
     const uint8_t* mrow = nullptr;
     if (MASK != MASK_NONE) {
@@ -238,10 +242,13 @@ fwd_f32_kernel(const FwdParams p)
         }
     };
 
-    const int n_tiles = (kv_end + BN - 1) / BN;
+    const int n_all = (kv_end + BN - 1) / BN;
+    // (tiles are numbered from 0 at key 0; a split work-group ends its range early)
+    const int n_tiles = p.n_split > 1 ? min(n_all, t_first + p.split_tiles) : n_all;
     // this wave needs tiles 0..t_last (causal rows never see later keys)
     int t_last = n_tiles - 1;
     if (CAUSAL) t_last = min(t_last, (wq0 + 31) / BN);
+    if (wq0 >= p.qL) t_last = -1;  // every row of this wave is past qL: it only helps stage tiles
 
     // K tile t -> LDS directly: 1 KiB block i by wave i % NW, lane l writing
     // slot 64i + l; pad slots are skipped, rows past kL repeat row kL - 1
@@ -328,7 +335,25 @@ fwd_f32_kernel(const FwdParams p)
         if (t + 1 < n_tiles) step(t + 1, Ks1, Vt1, Ks0, Vt0);
     }
 
-    if (qrow < p.qL) {
+    if (qrow < p.qL && p.n_split > 1) {
+        // one key range of a split launch: its normalised O and natural-log L
+        // (-inf when the range holds no allowed key), merged afterwards
+        const float inv = (l_run > 0.f) ? (DROP ? p.drop_scale : 1.f) / l_run : 0.f;
+        const int64_t rows = (int64_t)p.B * p.Hq * p.qL;
+        const int64_t row = ((int64_t)b * p.Hq + h) * p.qL + qrow;
+        float* orow = p.o_part + ((int64_t)split * rows + row) * D;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                if (32 * d + 8 * rq >= D) continue;
+                *(f32x4*)(orow + 32 * d + 8 * rq + 4 * g) =
+                    f32x4{o[d][4 * rq + 0], o[d][4 * rq + 1], o[d][4 * rq + 2], o[d][4 * rq + 3]} * inv;
+            }
+        if (g == 0)
+            p.l_part[(int64_t)split * rows + row] =
+                (l_run > 0.f) ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : -INFINITY;
+    } else if (qrow < p.qL) {
         // dropout's 1 / (1 - p) scales every kept term alike: it is applied here
         const float inv = (l_run > 0.f) ? (DROP ? p.drop_scale : 1.f) / l_run : 0.f;
         float* orow = (float*)p.o + b * p.o_s[0] + h * p.o_s[1] + (int64_t)qrow * p.o_s[2];
@@ -347,18 +372,124 @@ fwd_f32_kernel(const FwdParams p)
     }
 }
 
+// Merge of a split fp32 launch (one wave per query row): with L_s the
+// natural-log L of key range s, L = ln sum_s e^{L_s} and O = sum_s e^{L_s - L}
+// O_s, written through O's strides.  Ranges with no allowed key (L_s = -inf)
+// weigh 0; a row with none at all gets O = 0, L = 0.
+template <int D>
+__global__ void __launch_bounds__(256) merge_splits_f32_kernel(const FwdParams p)
+{
+    constexpr int NE = (D + 63) / 64;  // head-dim elements per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t rows = (int64_t)p.B * p.Hq * p.qL;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int i = (int)(row % p.qL);
+    const int64_t bh = row / p.qL;
+    const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+    float lmax = -INFINITY;
+    for (int s = lane; s < p.n_split; s += 64) lmax = fmaxf(lmax, p.l_part[s * rows + row]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, m));
+    float acc[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[e] = 0.f;
+    float sum = 0.f;
+    if (lmax != -INFINITY) {
+        for (int s = lane; s < p.n_split; s += 64) sum += __builtin_amdgcn_exp2f((p.l_part[s * rows + row] - lmax) * kLog2e);
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
+#pragma unroll 8
+        for (int s = 0; s < p.n_split; ++s) {
+            const float w = __builtin_amdgcn_exp2f((p.l_part[s * rows + row] - lmax) * kLog2e);
+            const float* src = p.o_part + (s * rows + row) * D;
+#pragma unroll
+            for (int e = 0; e < NE; ++e)
+                if (lane + 64 * e < D) acc[e] = __builtin_fmaf(w, src[lane + 64 * e], acc[e]);
+        }
+    }
+    const float inv = (sum > 0.f) ? 1.f / sum : 0.f;
+    float* orow = (float*)p.o + b * p.o_s[0] + h * p.o_s[1] + (int64_t)i * p.o_s[2];
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+        if (lane + 64 * e < D) orow[lane + 64 * e] = acc[e] * inv;
+    if (lane == 0) p.lse[row] = (sum > 0.f) ? lmax + __builtin_amdgcn_logf(sum) * kLn2 : 0.f;
+}
+
+// How many work-groups a query tile's key range is split over (1: none): a
+// grid that leaves more than half of the CUs idle while each work-group walks
+// a long key range (at least 2 kMinSplitTiles tiles) splits that range, up to
+// one full GPU of work-groups, at least kMinSplitTiles tiles each (a multiple
+// of 2, the K ring depth).
+template <bool CAUSAL, int BN>
+int split_plan_f32(const FwdParams& p, int64_t wgs, int* split_tiles)
+{
+    constexpr int kCUs = 256;
+    constexpr int kMinSplitTiles = 8;
+    const int kv_max = CAUSAL ? min(p.kL, p.qL) : p.kL;
+    const int n_kt = (kv_max + BN - 1) / BN;
+    *split_tiles = 0;
+    if (p.window > 0 || wgs * 2 > kCUs || n_kt < 2 * kMinSplitTiles) return 1;
+    const int64_t want = (int64_t)kCUs / wgs;  // one work-group per CU
+    const int by_len = n_kt / kMinSplitTiles;
+    const int s0 = (int)(want < by_len ? want : (int64_t)by_len);
+    if (s0 < 2) return 1;
+    int st = (n_kt + s0 - 1) / s0;
+    st = (st + 1) / 2 * 2;
+    *split_tiles = st;
+    return (n_kt + st - 1) / st;
+}
+
 template <int D, int MASK, bool CAUSAL, int NW, int BN, bool DROP = false>
 hipError_t launch_f32(const FwdParams& p, hipStream_t st, size_t* need = nullptr)
 {
-    if (need) {
-        *need = 0;  // never splits its key range
-        return hipSuccess;
-    }
+    // the kernel divides its grid index by n_split
+    if (p.n_split < 1) return hipErrorInvalidValue;
     FwdParams q = p;
     const int64_t wgs = (int64_t)p.n_qtiles * p.Hq * p.B;
-    q.pair_tiles = CAUSAL && grid_fits_at_once(wgs, 1);
-    hipLaunchKernelGGL((fwd_f32_kernel<D, MASK, CAUSAL, NW, BN, DROP>), dim3((unsigned)wgs), dim3(NW * 64), 0, st, q);
-    return hipGetLastError();
+    int split_tiles = 0;
+    const int n_split = split_plan_f32<CAUSAL, BN>(p, wgs, &split_tiles);
+    const int64_t rows = (int64_t)p.B * p.Hq * p.qL;
+    const size_t ws_bytes = n_split < 2 ? 0 : (size_t)n_split * rows * (D + 1) * sizeof(float);
+    if (need) {
+        *need = ws_bytes;
+        return hipSuccess;
+    }
+    if (n_split < 2) {
+        q.pair_tiles = CAUSAL && grid_fits_at_once(wgs, 1);
+        hipLaunchKernelGGL((fwd_f32_kernel<D, MASK, CAUSAL, NW, BN, DROP>), dim3((unsigned)wgs), dim3(NW * 64), 0, st,
+                           q);
+        return hipGetLastError();
+    }
+    // partials in the caller's scratch or from the library's stream-ordered
+    // pool (freed for reuse once the merge has read them); every partial the
+    // merge reads is written by this launch first
+    void* ws = p.ws;
+    hipError_t err = hipSuccess;
+    if (ws != nullptr) {
+        if (p.ws_bytes < ws_bytes) return hipErrorInvalidValue;
+    } else {
+        hipMemPool_t pool;
+        err = library_pool(&pool);
+        if (err != hipSuccess) return err;
+        err = hipMallocFromPoolAsync(&ws, ws_bytes, pool, st);
+        if (err != hipSuccess) return err;
+    }
+    q.o_part = (float*)ws;
+    q.l_part = q.o_part + (int64_t)n_split * rows * D;
+    q.n_split = n_split;
+    q.split_tiles = split_tiles;
+    q.pair_tiles = CAUSAL && grid_fits_at_once(wgs * n_split, 1);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, MASK, CAUSAL, NW, BN, DROP>), dim3((unsigned)(wgs * n_split)),
+                       dim3(NW * 64), 0, st, q);
+    err = hipGetLastError();
+    if (err == hipSuccess) {
+        hipLaunchKernelGGL((merge_splits_f32_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, q);
+        err = hipGetLastError();
+    }
+    if (p.ws != nullptr) return err;
+    const hipError_t ferr = hipFreeAsync(ws, st);
+    return err != hipSuccess ? err : ferr;
 }
 
 }  // namespace

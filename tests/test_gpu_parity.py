@@ -385,6 +385,41 @@ def test_key_range_split_over_work_groups(B, Hq, Hkv, qL, kL, D, kind, causal):
         assert np.all(O[0, Hq - 1, qL // 2] == 0) and L[0, Hq - 1, qL // 2] == 0
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,qL,kL,D,kind,causal", [
+    (1, 8, 2, 1, 4096, 128, "none", False),
+    (1, 8, 2, 16, 4100, 128, "none", False),
+    (2, 4, 4, 64, 3000, 64, "additive", False),
+    (1, 8, 8, 16, 4096, 32, "bool", False),
+    (1, 6, 3, 40, 5000, 96, "none", False),
+    (1, 2, 1, 1024, 2048, 128, "none", True),
+    (1, 2, 2, 1500, 1600, 80, "bool", True),
+    (1, 3, 1, 100, 2000, 256, "additive", False),
+], ids=lambda x: str(x))
+def test_key_range_split_over_work_groups_f32(B, Hq, Hkv, qL, kL, D, kind, causal):
+    """The fp32 kernel's key-range split: small grids with long key ranges,
+    fp32 partials merged by L = ln sum e^{L_s}; empty causal ranges and a row
+    with no allowed key in any range."""
+    print(f"[case] f32 split B={B} Hq={Hq} Hkv={Hkv} qL={qL} kL={kL} D={D} mask={kind} causal={causal}", flush=True)
+    q, k, v = _rand((B, Hq, qL, D), F32, 45), _rand((B, Hkv, kL, D), F32, 46), _rand((B, Hkv, kL, D), F32, 47)
+    mask = None
+    if kind != "none":
+        rng = np.random.default_rng(48)
+        masked = W.draw_masked(rng, (B, Hq, qL, kL), 0.3)
+        masked[0, Hq - 1, qL // 2, :] = True  # no allowed key in any range
+        if kind == "bool":
+            mask = torch.from_numpy((~masked).astype(np.uint8))
+        else:
+            m = rng.standard_normal(masked.shape).astype(np.float32)
+            m[masked] = -np.inf
+            mask = torch.from_numpy(m)
+    scale = 1 / math.sqrt(D)
+    O, L, _ = run_gpu(q, k, v, mask, causal=causal, scale=scale)
+    Oref, Lref = run_oracle(q, k, v, mask, causal=causal, scale=scale)
+    assert_parity(O, L, Oref, Lref, "f32", f"f32 split qL={qL} kL={kL} D={D} {kind} causal={causal}")
+    if kind != "none":
+        assert np.all(O[0, Hq - 1, qL // 2] == 0) and L[0, Hq - 1, qL // 2] == 0
+
+
 @pytest.mark.parametrize("Hq,Hkv,qL,kL,D,kind,causal", [
     (8, 4, 1, 4096, 128, "none", False),
     (8, 2, 17, 3000, 128, "additive", False),

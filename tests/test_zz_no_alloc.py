@@ -21,6 +21,8 @@ CASES = [
     ("decode_split32", W.SPLIT_KV[0], W.Workload("decode_small", "bf16", 1, 8, 2, 16, 8192, 128, 0.088, seed=61)),
     ("masked_d256_split4", W.C5, W.Workload("masked_d256_small", "bf16", 1, 4, 4, 512, 3072, 256, 0.0625,
                                             mask_kind="additive", p_masked=0.2, seed=62)),
+    ("f32_decode_split", W.Workload("f32_decode", "f32", 1, 8, 2, 16, 16384, 128, 0.088, seed=65),
+     W.Workload("f32_decode_small", "f32", 1, 4, 2, 8, 4096, 64, 0.125, causal=False, seed=66)),
     ("unsplit_causal_gqa", W.Workload("gqa_300", "bf16", 2, 4, 2, 300, 300, 64, 0.125, causal=True, seed=63),
      W.Workload("gqa_100", "bf16", 1, 4, 2, 100, 120, 64, 0.125, causal=True, seed=64)),
 ]

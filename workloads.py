@@ -103,6 +103,8 @@ HEAD_DIMS = [
 SPLIT_KV = [
     Workload("decode_bf16_d128_32k", "bf16", 1, 32, 8, 16, 32768, 128, 1 / math.sqrt(128), seed=60,
              note="16 query rows over 32768 keys, bf16 D=128 (K/V-read bound)"),
+    Workload("decode_f32_d128_32k", "f32", 1, 32, 8, 16, 32768, 128, 1 / math.sqrt(128), seed=61,
+             note="16 query rows over 32768 keys, fp32 D=128 (K/V-read bound)"),
 ]
 
 # The headline shape with dropout on the attention weights (rate 0.1).
