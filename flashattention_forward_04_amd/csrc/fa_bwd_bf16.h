@@ -510,7 +510,7 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t st)
 #define FA_BWD_D64_CFG 4, 64, 2, 4, 64, 2
 #endif
 #ifndef FA_BWD_D128_CFG
-#define FA_BWD_D128_CFG 4, 32, 2, 4, 64, 1
+#define FA_BWD_D128_CFG 4, 32, 2, 4, 32, 2
 #endif
 
 #define FA_BWD_VARIANT(D, MASK, CAUSAL, NAME, QNW, BN, QWPE, KNW, BQ, KWPE) \

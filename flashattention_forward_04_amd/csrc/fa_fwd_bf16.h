@@ -114,6 +114,12 @@ constexpr float kRescaleSlack = 8.f;
 #define FA_SCHED_S 4
 #endif
 
+// Walk the key range of causal grids that fit at once in two halves per
+// work-group (see launch_bf16_any).
+#ifndef FA_KEY_HALVES
+#define FA_KEY_HALVES 1
+#endif
+
 // Split long key ranges of small grids over work-groups (see launch_bf16).
 #ifndef FA_SPLIT_KV
 #define FA_SPLIT_KV 1
@@ -154,13 +160,23 @@ __device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
 //
 // K/V tiles are loaded straight from global memory into LDS (no registers),
 // round a ring of NB buffers, with one barrier per tile.
-template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB, bool DROP = false>
+//
+// KSPLIT (key halves): the NW waves form two halves of NW / 2 waves on the
+// same NW / 2 row blocks.  Half 0 walks the first half of the work-group's
+// key tiles and half 1 the second, each round its own ring of LDS buffers,
+// so a long causal row block takes half as many steps.  At the end the two
+// softmax states (m, l, O) of each row are merged through LDS -- the same
+// combination the online softmax applies between key blocks.
+template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB, bool DROP = false,
+          bool KSPLIT = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fwd_bf16_kernel(const FwdParams p)
 {
     static_assert(SCHED == 0 || SCHED == 1, "schedule: 0 plain, 1 pipelined");
     constexpr bool PIPE = SCHED != 0;  // next tile's scores formed during this tile's softmax
-    constexpr int BM = NW * 32;       // query rows per work-group
+    constexpr int NH = KSPLIT ? 2 : 1;  // key halves
+    constexpr int WH = NW / NH;         // waves per half; the halves share the query rows
+    constexpr int BM = WH * 32;         // query rows per work-group
     using KL = TileLayout<D + 8>;     // K tile layout in LDS
     using VL = TileLayout<D + 32>;    // V tile layout in LDS
     // tiles are padded to whole 1 KiB blocks: one direct load of a wave
@@ -184,7 +200,11 @@ fwd_bf16_kernel(const FwdParams p)
     // NB buffers each for K and V, as separate arrays so that the compiler
     // can tell the buffer being loaded from the ones being read
     static_assert(NB == 2 || NB == 4, "ring depth");
-    constexpr int KT2 = NB > 2 ? KTILE : 1, VT2 = NB > 2 ? VTILE : 1;
+    // key halves: buffers 0-1 are half 0's ring, 2-3 half 1's; the merge
+    // passes each row block's state through one V buffer
+    static_assert(!KSPLIT || (NB == 2 && !DROP && NW % 2 == 0 && WH <= 4 &&
+                              (1024 * ((D + 31) / 32) + 128) * 4 <= VTILE * 2), "key halves");
+    constexpr int KT2 = (NB > 2 || KSPLIT) ? KTILE : 1, VT2 = (NB > 2 || KSPLIT) ? VTILE : 1;
     __shared__ __attribute__((aligned(1024))) uint16_t Ks0[KTILE];
     __shared__ __attribute__((aligned(1024))) uint16_t Ks1[KTILE];
     __shared__ __attribute__((aligned(1024))) uint16_t Ks2[KT2];
@@ -193,22 +213,6 @@ fwd_bf16_kernel(const FwdParams p)
     __shared__ __attribute__((aligned(1024))) uint16_t Vs1[VTILE];
     __shared__ __attribute__((aligned(1024))) uint16_t Vs2[VT2];
     __shared__ __attribute__((aligned(1024))) uint16_t Vs3[VT2];
-    auto kbuf = [&](auto i_c) __attribute__((always_inline)) -> uint16_t* {
-        constexpr int I = decltype(i_c)::value;
-        return I == 0 ? Ks0 : I == 1 ? Ks1 : I == 2 ? Ks2 : Ks3;
-    };
-    auto vbuf = [&](auto i_c) __attribute__((always_inline)) -> uint16_t* {
-        constexpr int I = decltype(i_c)::value;
-        return I == 0 ? Vs0 : I == 1 ? Vs1 : I == 2 ? Vs2 : Vs3;
-    };
-    // the same by a (fully unrolled, hence constant) index
-    auto kbuf_dyn = [&](int i) __attribute__((always_inline)) -> uint16_t* {
-        return i == 0 ? Ks0 : i == 1 ? Ks1 : i == 2 ? Ks2 : Ks3;
-    };
-    auto vbuf_dyn = [&](int i) __attribute__((always_inline)) -> uint16_t* {
-        return i == 0 ? Vs0 : i == 1 ? Vs1 : i == 2 ? Vs2 : Vs3;
-    };
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // the wave index is uniform across the wave; saying so keeps the per-wave
@@ -216,6 +220,29 @@ fwd_bf16_kernel(const FwdParams p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r32 = lane & 31;
     const int g = lane >> 5;
+    const int half = KSPLIT ? wave / WH : 0;  // key half of this wave (0 without KSPLIT)
+    const int wrow = KSPLIT ? wave % WH : wave;  // row block of this wave
+
+    // buffer i of this wave's ring
+    auto kbuf = [&](auto i_c) __attribute__((always_inline)) -> uint16_t* {
+        constexpr int I = decltype(i_c)::value;
+        if constexpr (KSPLIT) return half ? (I == 0 ? Ks2 : Ks3) : (I == 0 ? Ks0 : Ks1);
+        return I == 0 ? Ks0 : I == 1 ? Ks1 : I == 2 ? Ks2 : Ks3;
+    };
+    auto vbuf = [&](auto i_c) __attribute__((always_inline)) -> uint16_t* {
+        constexpr int I = decltype(i_c)::value;
+        if constexpr (KSPLIT) return half ? (I == 0 ? Vs2 : Vs3) : (I == 0 ? Vs0 : Vs1);
+        return I == 0 ? Vs0 : I == 1 ? Vs1 : I == 2 ? Vs2 : Vs3;
+    };
+    // the same by a (fully unrolled, hence constant) index
+    auto kbuf_dyn = [&](int i) __attribute__((always_inline)) -> uint16_t* {
+        if (KSPLIT) i += 2 * half;
+        return i == 0 ? Ks0 : i == 1 ? Ks1 : i == 2 ? Ks2 : Ks3;
+    };
+    auto vbuf_dyn = [&](int i) __attribute__((always_inline)) -> uint16_t* {
+        if (KSPLIT) i += 2 * half;
+        return i == 0 ? Vs0 : i == 1 ? Vs1 : i == 2 ? Vs2 : Vs3;
+    };
 
     // ---- which (query tile, head, batch) this work-group owns ----
     // Normally one query head and NW * 32 consecutive rows.  With head_pack
@@ -252,7 +279,7 @@ fwd_bf16_kernel(const FwdParams p)
         const int qt = CAUSAL ? causal_tile(id, p.n_qtiles, p.pair_tiles) : id;
         q0 = qt * BM;
         hk = h / p.group;
-        wq0 = q0 + wave * 32;  // first query row of this wave
+        wq0 = q0 + wrow * 32;  // first query row of this wave
     }
     const int qrow = wq0 + r32;  // this lane's query row
 
@@ -281,8 +308,14 @@ fwd_bf16_kernel(const FwdParams p)
     // window starts the range at the tile of the first row's first key.
     const bool win = CAUSAL && p.window > 0;
     const int n_all = (kv_end + BN - 1) / BN;
-    const int tb = (win ? max(0, q0 - p.window + 1) / BN : 0) + split * p.split_tiles;
-    const int n_tiles = max(0, (p.n_split > 1 ? min(n_all, tb + p.split_tiles) : n_all) - tb);
+    const int tb_wg = (win ? max(0, q0 - p.window + 1) / BN : 0) + split * p.split_tiles;
+    const int n_wg = max(0, (p.n_split > 1 ? min(n_all, tb_wg + p.split_tiles) : n_all) - tb_wg);
+    // key halves: half 0 takes tiles [0, nh) of the range, half 1 the rest;
+    // both run nh steps (the barriers are shared)
+    const int nh = KSPLIT ? (n_wg + 1) / 2 : n_wg;
+    const int tb = tb_wg + (half ? nh : 0);                            // this wave's first tile
+    const int n_tiles = KSPLIT ? (half ? n_wg - nh : nh) : n_wg;      // and how many it takes
+    const int n_steps = nh;                                            // loop steps of the work-group
     // this wave needs tiles 0..t_last (a prefix: causal rows never see later keys)
     int t_last = n_tiles - 1;
     if (CAUSAL) t_last = min(t_last, (wq0 + 31) / BN - tb);
@@ -316,15 +349,15 @@ fwd_bf16_kernel(const FwdParams p)
     // within a tile (row * stride + chunk * 8) are computed once, so a full
     // tile's load address is one add; only the tail tile (rows past kL,
     // clamped) recomputes them.
-    constexpr int KIT = (KINS + NW - 1) / NW;  // direct loads per wave per K tile (at most)
-    constexpr int VIT = (VINS + NW - 1) / NW;
+    constexpr int KIT = (KINS + WH - 1) / WH;  // direct loads per wave per K tile (at most)
+    constexpr int VIT = (VINS + WH - 1) / WH;
     int64_t koff[KIT], voff[VIT];
     auto slot_offsets = [&](int64_t* off, int64_t stride, auto spr_c, auto nins_c) __attribute__((always_inline)) {
         constexpr int SPR = decltype(spr_c)::value;
         constexpr int NINS = decltype(nins_c)::value;
 #pragma unroll
-        for (int k = 0; k < (NINS + NW - 1) / NW; ++k) {
-            const int slot = 64 * (wave + k * NW) + lane;
+        for (int k = 0; k < (NINS + WH - 1) / WH; ++k) {
+            const int slot = 64 * (wrow + k * WH) + lane;
             off[k] = (int64_t)(slot / SPR) * stride + (slot % SPR) * 8;
         }
     };
@@ -338,9 +371,9 @@ fwd_bf16_kernel(const FwdParams p)
             constexpr bool FULL = decltype(full_c)::value;
             const uint16_t* tbase = gbase + (int64_t)j0 * stride;
 #pragma unroll
-            for (int k = 0; k < (NINS + NW - 1) / NW; ++k) {
-                const int i = wave + k * NW;
-                if (NINS % NW != 0 && i >= NINS) break;
+            for (int k = 0; k < (NINS + WH - 1) / WH; ++k) {
+                const int i = wrow + k * WH;
+                if (NINS % WH != 0 && i >= NINS) break;
                 const int slot = 64 * i + lane;
                 const int row = slot / SPR;
                 const int ch = slot % SPR;
@@ -662,7 +695,7 @@ fwd_bf16_kernel(const FwdParams p)
     constexpr int PK = PIPE ? NB : NB - 1;  // load-ahead distance of K
     constexpr int PV = NB - 1;              // load-ahead distance of V
     // loads this wave issues per tile (the fewest any wave issues)
-    constexpr int kLoadsPerStep = KINS / NW + VINS / NW;
+    constexpr int kLoadsPerStep = KINS / WH + VINS / WH;
     // At the end of step t, what step t+1 reads was issued at step t+2-NB or
     // earlier, so the loads of the last NB-2 steps may stay in flight (when
     // all of them were issued; near the end everything is waited for).
@@ -712,19 +745,52 @@ fwd_bf16_kernel(const FwdParams p)
     wait_loads();
     __syncthreads();
     if (PIPE) {
-        if (t_last >= 0) score_products(sa, Ks0, 0, NP);
+        if (t_last >= 0) score_products(sa, kbuf_dyn(0), 0, NP);
         __syncthreads();  // K of tile 0 is read before tile NB replaces it
     }
-    for (int t0 = 0; t0 < n_tiles; t0 += NB) {
+    for (int t0 = 0; t0 < n_steps; t0 += NB) {
         step(t0, std::integral_constant<int, 0>{});
-        if (t0 + 1 < n_tiles) step(t0 + 1, std::integral_constant<int, 1>{});
+        if (t0 + 1 < n_steps) step(t0 + 1, std::integral_constant<int, 1>{});
         if (NB > 2) {
-            if (t0 + 2 < n_tiles) step(t0 + 2, std::integral_constant<int, 2 % NB>{});
-            if (t0 + 3 < n_tiles) step(t0 + 3, std::integral_constant<int, 3 % NB>{});
+            if (t0 + 2 < n_steps) step(t0 + 2, std::integral_constant<int, 2 % NB>{});
+            if (t0 + 3 < n_steps) step(t0 + 3, std::integral_constant<int, 3 % NB>{});
+        }
+    }
+
+    if constexpr (KSPLIT) {
+        // The halves' softmax states meet in LDS: wave wrow of half 1 leaves
+        // its (O^T, m, l) in V buffer wrow (lane-major, so each lane reads
+        // back its own values), and wave wrow of half 0 -- the same rows and
+        // the same accumulator layout -- folds it in: m = max(m0, m1),
+        // l = l0 2^(m0 - m) + l1 2^(m1 - m), O likewise (a half with no
+        // allowed key, m = -inf, weighs 0).
+        __syncthreads();  // every wave is past its last read of the K/V buffers; no load is in flight
+        float* xb = (float*)(wrow == 0 ? Vs0 : wrow == 1 ? Vs1 : wrow == 2 ? Vs2 : Vs3);
+        if (half == 1) {
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xb[(d * 16 + r) * 64 + lane] = o[d][r];
+            xb[ND * 1024 + lane] = m_run;
+            xb[ND * 1024 + 64 + lane] = l_run;
+        }
+        __syncthreads();
+        if (half == 0) {
+            const float m1 = xb[ND * 1024 + lane], l1 = xb[ND * 1024 + 64 + lane];
+            const float m = fmaxf(m_run, m1);
+            const float c0 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+            const float c1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[d][r] = __builtin_fmaf(o[d][r], c0, xb[(d * 16 + r) * 64 + lane] * c1);
+            l_run = __builtin_fmaf(l_run, c0, l1 * c1);
+            m_run = m;
         }
     }
 
     // ---- epilogue: O = O / l, L = (m + log2 l) ln2 (O = 0, L = 0 if no key) ----
+    if (KSPLIT && half != 0) return;  // half 0 writes the merged rows
     if (qrow < p.qL && head_ok && p.n_split > 1) {
         // one key range of a split launch: normalised fp32 O and natural-log
         // L of this range (-inf when it holds no allowed key)
@@ -849,17 +915,19 @@ int split_plan(const FwdParams& p, int64_t wgs, int wgs_per_cu_, int* split_tile
     return (n_kt + st - 1) / st;
 }
 
-template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB, bool DROP = false>
+template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB, bool DROP = false,
+          bool KSPLIT = false>
 hipError_t launch_bf16(const FwdParams& p, hipStream_t st, size_t* need = nullptr)
 {
     // the work-group kernel divides its grid index by n_split
     if (p.n_split < 1) return hipErrorInvalidValue;
-    constexpr int kWgsPerCu = wgs_per_cu<D, NW, BN, WPE, NB>();
+    // (key halves: twice the LDS ring, and never a split over work-groups)
+    constexpr int kWgsPerCu = wgs_per_cu<D, NW, BN, WPE, KSPLIT ? 2 * NB : NB>();
     FwdParams q = p;
     const int64_t wgs = p.head_pack ? (int64_t)p.n_qtiles * ((p.group + NW - 1) / NW) * p.Hkv * p.B
                                     : (int64_t)p.n_qtiles * p.Hq * p.B;
     int split_tiles = 0;
-    const int n_split = split_plan<CAUSAL, BN, NB>(p, wgs, kWgsPerCu, &split_tiles);
+    const int n_split = KSPLIT ? 1 : split_plan<CAUSAL, BN, NB>(p, wgs, kWgsPerCu, &split_tiles);
     const int64_t rows = (int64_t)p.B * p.Hq * p.qL;
     const size_t ws_bytes = n_split < 2 ? 0 : (size_t)n_split * rows * (D + 1) * sizeof(float);
     if (need) {
@@ -868,8 +936,8 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t st, size_t* need = nullpt
     }
     if (n_split < 2) {
         q.pair_tiles = CAUSAL && grid_fits_at_once(wgs, kWgsPerCu);
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB, DROP>), dim3((unsigned)wgs),
-                           dim3(NW * 64), 0, st, q);
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB, DROP, KSPLIT>),
+                           dim3((unsigned)wgs), dim3(NW * 64), 0, st, q);
         return hipGetLastError();
     }
     // partials in the caller's scratch, or from the library's stream-ordered
@@ -892,8 +960,8 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t st, size_t* need = nullpt
     q.n_split = n_split;
     q.split_tiles = split_tiles;
     q.pair_tiles = CAUSAL && grid_fits_at_once(wgs * n_split, kWgsPerCu);
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB, DROP>), dim3((unsigned)(wgs * n_split)),
-                       dim3(NW * 64), 0, st, q);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB, DROP, KSPLIT>),
+                       dim3((unsigned)(wgs * n_split)), dim3(NW * 64), 0, st, q);
     err = hipGetLastError();
     if (err == hipSuccess) {
         hipLaunchKernelGGL((merge_splits_bf16_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, q);
@@ -1489,6 +1557,18 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st, size_t* need = nu
             q.n_qtiles = (p.qL + 127) / 128;
             return launch_bf16<D, MASK, CAUSAL, 4, 32, 2, 0, 2>(q, st, need);
         }
+    }
+    if constexpr (FA_KEY_HALVES && CAUSAL && NW <= 4 && BN >= 64 && NB == 2) {
+        // Causal grids that fit on the GPU at once but are too large to split
+        // over work-groups (e.g. 2 x 16 heads x 2048 rows at D = 64): a long
+        // row block would run its key tiles alone at the end, so each
+        // work-group walks its key range in two halves side by side (twice
+        // the waves, the same rows) and merges them.
+        const int64_t wgs = (int64_t)p.n_qtiles * p.Hq * p.B;
+        const int n_kt = (min(p.kL, p.qL) + BN - 1) / BN;
+        if (p.window == 0 && p.head_pack == 0 && wgs * 2 > 256 && n_kt >= 8 &&
+            grid_fits_at_once(wgs, wgs_per_cu<D, NW, BN, WPE, NB>()))
+            return launch_bf16<D, MASK, CAUSAL, 2 * NW, BN, WPE, SCHED, NB, false, true>(p, st, need);
     }
     return launch_bf16<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB>(p, st, need);
 }

@@ -618,3 +618,33 @@ def test_split_launch_leaves_the_default_pool_alone():
     O, L, _ = run_gpu(q, k, v, None, causal=w.causal, scale=w.scale)
     assert np.all(np.isfinite(O))
     assert _default_pool_release_threshold() == before
+
+
+@pytest.mark.parametrize("D", [16, 32, 48, 64])
+@pytest.mark.parametrize("kind", ["none", "additive", "bool"])
+@pytest.mark.parametrize("B,Hq,Hkv,qL,kL", [(1, 40, 8, 600, 600), (2, 24, 6, 700, 650), (1, 36, 4, 1100, 1025)],
+                         ids=lambda x: str(x))
+def test_causal_key_halves(D, kind, B, Hq, Hkv, qL, kL):
+    """Causal grids that fit on the GPU at once but are too large to split over
+    work-groups take the work-group kernel with its key range walked in two
+    halves side by side, merged through LDS (odd tile counts leave half 1 one
+    tile short, or empty on the first row block)."""
+    print(f"[case] key halves B={B} Hq={Hq} Hkv={Hkv} qL={qL} kL={kL} D={D} mask={kind}", flush=True)
+    q, k, v = _rand((B, Hq, qL, D), BF16, 51), _rand((B, Hkv, kL, D), BF16, 52), _rand((B, Hkv, kL, D), BF16, 53)
+    mask = None
+    if kind != "none":
+        rng = np.random.default_rng(54)
+        masked = W.draw_masked(rng, (B, Hq, qL, kL), 0.3)
+        masked[0, Hq - 1, qL // 2, :] = True  # a row with no allowed key
+        if kind == "bool":
+            mask = torch.from_numpy((~masked).astype(np.uint8))
+        else:
+            m = rng.standard_normal(masked.shape).astype(np.float32)
+            m[masked] = -np.inf
+            mask = torch.from_numpy(m).to(BF16)
+    scale = 1 / math.sqrt(D)
+    O, L, _ = run_gpu(q, k, v, mask, causal=True, scale=scale)
+    Oref, Lref = run_oracle(q, k, v, mask, causal=True, scale=scale)
+    assert_parity(O, L, Oref, Lref, "bf16", f"key halves qL={qL} kL={kL} D={D} {kind}")
+    if kind != "none":
+        assert np.all(O[0, Hq - 1, qL // 2] == 0) and L[0, Hq - 1, qL // 2] == 0
