@@ -264,7 +264,9 @@ def summarize(prof_dir, w, commands):
             f"{mops} x 512; LDS conflict = SQ_LDS_BANK_CONFLICT / ({N_CU} CUs x cycles).  Timings under --pmc "
             "are serialised dispatches, so they differ from the trace above.",
             "",
-            f"Averages over the {len(timed)} timed dispatches: clock {avg['ghz']:.3f} GHz, "
+            f"Averages over the {len(timed)} timed dispatches: clock {avg['ghz']:.3f} GHz"
+            + (" (a dispatch this short is shorter than the counter window, so this overstates the clock and "
+               "understates the busy fractions)" if avg["us"] < 150 else "") + ", "
             f"{avg['cycles'] / 1e6:.3f} M cycles, MFMA busy {avg['mfma_busy']:.3f}, CU busy {avg['cu_busy']:.3f}, "
             f"{avg['valu_per_wave']:.0f} VALU and {avg['trans_per_wave']:.0f} transcendental instructions per wave, "
             f"matrix FLOP {avg['mfma_flop']:.4g} ({avg['mfma_flop'] / flops:.3f}x the algorithmic {flops:.4g}), "
