@@ -130,6 +130,19 @@ inline bool grid_fits_at_once(int64_t wgs, int wgs_per_cu) {
 // compiler-tracked direct load and index no register array at run time (a
 // test scans the built code object for any other M0 use).  The s_nop is the
 // wait the hardware needs between writing M0 and the load that reads it.
+// The same from a wave-uniform base (an SGPR pair) plus this lane's 32-bit
+// byte offset: half the address bytes a 64-bit per-lane address takes, which
+// makes the load cheaper to issue.
+__device__ __forceinline__ void lds_dma16_so(const void* gbase, uint32_t byte_off, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(byte_off), "s"(gbase), "s"(lds_base)
+        : "memory");
+}
+
 __device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_base) {
     asm volatile(
         "s_mov_b32 m0, %1\n\t"

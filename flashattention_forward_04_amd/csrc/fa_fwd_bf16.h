@@ -351,25 +351,34 @@ fwd_bf16_kernel(const FwdParams p)
     // clamped) recomputes them.
     constexpr int KIT = (KINS + WH - 1) / WH;  // direct loads per wave per K tile (at most)
     constexpr int VIT = (VINS + WH - 1) / WH;
-    int64_t koff[KIT], voff[VIT];
-    auto slot_offsets = [&](int64_t* off, int64_t stride, auto spr_c, auto nins_c) __attribute__((always_inline)) {
+    // (32-bit byte offsets within a tile: a full tile takes them when BN rows
+    // of the larger stride fit in 31 bits, else the per-slot path)
+    const bool off32 = (int64_t)BN * max(p.k_s[2], p.v_s[2]) * 2 < ((int64_t)1 << 31);
+    uint32_t koff[KIT], voff[VIT];
+    auto slot_offsets = [&](uint32_t* off, int64_t stride, auto spr_c, auto nins_c) __attribute__((always_inline)) {
         constexpr int SPR = decltype(spr_c)::value;
         constexpr int NINS = decltype(nins_c)::value;
 #pragma unroll
         for (int k = 0; k < (NINS + WH - 1) / WH; ++k) {
             const int slot = 64 * (wrow + k * WH) + lane;
-            off[k] = (int64_t)(slot / SPR) * stride + (slot % SPR) * 8;
+            off[k] = (uint32_t)(((int64_t)(slot / SPR) * stride + (slot % SPR) * 8) * 2);
         }
     };
     slot_offsets(koff, p.k_s[2], std::integral_constant<int, KSPR>{}, std::integral_constant<int, KINS>{});
     slot_offsets(voff, p.v_s[2], std::integral_constant<int, VSPR>{}, std::integral_constant<int, VINS>{});
-    auto issue_tile = [&](const uint16_t* gbase, int64_t stride, int j0, uint16_t* lds, const int64_t* off,
+    auto issue_tile = [&](const uint16_t* gbase, int64_t stride, int j0, uint16_t* lds, const uint32_t* off,
                           auto spr_c, auto nins_c) __attribute__((always_inline)) {
         constexpr int SPR = decltype(spr_c)::value;
         constexpr int NINS = decltype(nins_c)::value;
         auto all_slots = [&](auto full_c) __attribute__((always_inline)) {
             constexpr bool FULL = decltype(full_c)::value;
-            const uint16_t* tbase = gbase + (int64_t)j0 * stride;
+            // the tile's base is the same for every lane: keep it in SGPRs
+            const uint64_t tb64 = (uint64_t)(size_t)(gbase + (int64_t)j0 * stride);
+            // (readfirstlane returns int: each half goes through uint32_t so
+            // that the low half is zero-extended, not sign-extended)
+            const uint32_t tb_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(tb64 >> 32));
+            const uint32_t tb_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)tb64);
+            const uint16_t* tbase = (const uint16_t*)(size_t)(((uint64_t)tb_hi << 32) | (uint64_t)tb_lo);
 #pragma unroll
             for (int k = 0; k < (NINS + WH - 1) / WH; ++k) {
                 const int i = wrow + k * WH;
@@ -379,8 +388,11 @@ fwd_bf16_kernel(const FwdParams p)
                 const int ch = slot % SPR;
                 if (ch < D / 8 && row < BN) {
                     const uint16_t* src =
-                        FULL ? tbase + off[k] : gbase + (int64_t)min(j0 + row, p.kL - 1) * stride + ch * 8;
-                    if (MASK == MASK_NONE) {
+                        FULL ? (const uint16_t*)((const char*)tbase + off[k])
+                             : gbase + (int64_t)min(j0 + row, p.kL - 1) * stride + ch * 8;
+                    if (MASK == MASK_NONE && FULL) {
+                        lds_dma16_so(tbase, off[k], (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(lds + 512 * i));
+                    } else if (MASK == MASK_NONE) {
                         lds_dma16(src, (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(lds + 512 * i));
                     } else {
                         // the masked kernels load the mask with ordinary
@@ -394,7 +406,7 @@ fwd_bf16_kernel(const FwdParams p)
                 }
             }
         };
-        if (j0 + BN <= p.kL)
+        if (j0 + BN <= p.kL && off32)
             all_slots(std::true_type{});
         else
             all_slots(std::false_type{});
@@ -1621,10 +1633,10 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st, size_t* need = nu
 #define FA_BF16_D96_MASKED_CFG 8, 64, 2, 0, 2
 #endif
 #ifndef FA_BF16_D256_CFG
-#define FA_BF16_D256_CFG 4, 32, 1, 0, 2
+#define FA_BF16_D256_CFG 4, 32, 1, 1, 2
 #endif
 #ifndef FA_BF16_D256_MASKED_CFG
-#define FA_BF16_D256_MASKED_CFG 4, 32, 1, 0, 2
+#define FA_BF16_D256_MASKED_CFG 4, 32, 1, 1, 2
 #endif
 
 #define FA_BF16_VARIANT(D, MASK, CAUSAL, NAME, NW, BN, WPE, SCHED, NB) \
