@@ -803,24 +803,60 @@ fwd_bf16_kernel(const FwdParams p)
 
     // ---- epilogue: O = O / l, L = (m + log2 l) ln2 (O = 0, L = 0 if no key) ----
     if (KSPLIT && half != 0) return;  // half 0 writes the merged rows
-    if (qrow < p.qL && head_ok && p.n_split > 1) {
+    if (p.n_split > 1) {
         // one key range of a split launch: normalised fp32 O and natural-log
         // L of this range (-inf when it holds no allowed key)
         // dropout's 1 / (1 - p) scales every kept term alike: it is applied here
         const float inv = (l_run > 0.f) ? (DROP ? p.drop_scale : 1.f) / l_run : 0.f;
         const int64_t rows = (int64_t)p.B * p.Hq * p.qL;
-        const int64_t row = ((int64_t)b * p.Hq + h) * p.qL + qrow;
-        float* orow = p.o_part + ((int64_t)split * rows + row) * D;
+        const bool row_ok = qrow < p.qL && head_ok;
+        // A lane's O^T registers hold 4 consecutive head-dim elements of one
+        // row per quad, so a store straight from them writes 32 bytes of
+        // each of 32 rows, and the partial cache lines cost HBM writes well
+        // beyond their bytes.  Each wave instead passes its rows through a
+        // 32 x XP float region of the (by now idle) K/V buffers, one 32-column
+        // block at a time, and each store then covers whole 128-byte lines
+        // of four rows.
+        constexpr int XP = 36;                        // region row pitch, floats
+        constexpr int XE = 32 * XP * 2;               // region size in 16-bit elements
+        constexpr int RK = KTILE / XE, RV = VTILE / XE;
+        constexpr bool XPOSE = 2 * RK + 2 * RV >= NW;  // (every wave gets a region)
+        if constexpr (XPOSE) {
+            __syncthreads();  // every wave is past its last read of the K/V buffers
+            const int w = wave;
+            float* xs = (float*)(w < RK             ? Ks0 + w * XE
+                                 : w < 2 * RK       ? Ks1 + (w - RK) * XE
+                                 : w < 2 * RK + RV  ? Vs0 + (w - 2 * RK) * XE
+                                                    : Vs1 + (w - 2 * RK - RV) * XE);
+            const int64_t row0 = ((int64_t)b * p.Hq + h) * p.qL + wq0;  // this wave's first row
 #pragma unroll
-        for (int d = 0; d < ND; ++d)
+            for (int d = 0; d < ND; ++d) {
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                if (32 * d + 8 * rq >= D) continue;
-                *(f32x4*)(orow + 32 * d + 8 * rq + 4 * g) =
-                    f32x4{o[d][4 * rq + 0], o[d][4 * rq + 1], o[d][4 * rq + 2], o[d][4 * rq + 3]} * inv;
+                for (int rq = 0; rq < 4; ++rq)
+                    *(f32x4*)(xs + r32 * XP + 8 * rq + 4 * g) =
+                        f32x4{o[d][4 * rq + 0], o[d][4 * rq + 1], o[d][4 * rq + 2], o[d][4 * rq + 3]} * inv;
+                // lane l reads columns 4 (l % 8) .. +3 of rows 8 i + l / 8
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rr = 8 * i + (lane >> 3), c4 = 4 * (lane & 7);
+                    const f32x4 v = *(const f32x4*)(xs + rr * XP + c4);
+                    if (32 * d + c4 < D && wq0 + rr < p.qL && head_ok)
+                        *(f32x4*)(p.o_part + ((int64_t)split * rows + row0 + rr) * D + 32 * d + c4) = v;
+                }
             }
-        if (g == 0)
-            p.l_part[(int64_t)split * rows + row] =
+        } else if (row_ok) {
+            float* orow = p.o_part + ((int64_t)split * rows + ((int64_t)b * p.Hq + h) * p.qL + qrow) * D;
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    if (32 * d + 8 * rq >= D) continue;
+                    *(f32x4*)(orow + 32 * d + 8 * rq + 4 * g) =
+                        f32x4{o[d][4 * rq + 0], o[d][4 * rq + 1], o[d][4 * rq + 2], o[d][4 * rq + 3]} * inv;
+                }
+        }
+        if (row_ok && g == 0)
+            p.l_part[(int64_t)split * rows + ((int64_t)b * p.Hq + h) * p.qL + qrow] =
                 (l_run > 0.f) ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : -INFINITY;
     } else if (qrow < p.qL && head_ok) {
         // dropout's 1 / (1 - p) scales every kept term alike: it is applied here
