@@ -581,7 +581,7 @@ def main():
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}
     roof.update({"traffic": recorded_traffic(w), "kernel_avg_us": round(kern_avg_ms * 1e3, 2)})
     metric = ("attention fwd TFLOP/s + % MFMA peak, bf16 D=128 causal qL=kL=8192" if w is W.HEADLINE
-              else f"attention fwd TFLOP/s, {w.name}")
+              else f"attention {'bwd' if w.backward else 'fwd'} TFLOP/s, {w.name}")
     res = {
         "metric": metric,
         "value": round(value, 2),

@@ -504,6 +504,7 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
     p.group = H_q / H_kv;
     p.scale = scale;
     p.scale_log2 = scale * 1.4426950408889634f;
+    p.kv_split = 1;  // the dK/dV grid divides its index by it: never 0 (the launcher may raise it)
     if (mask_kind != FA_MASK_NONE) {
         const int mesz = mask_kind == FA_MASK_BOOL ? 1 : 2;
         p.mask_vec = aligned(mask, (uintptr_t)4 * mesz) && kL % 4 == 0;

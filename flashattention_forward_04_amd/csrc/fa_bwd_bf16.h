@@ -321,10 +321,16 @@ bwd_dkdv_kernel(const BwdParams p)
     const int r32 = lane & 31, g = lane >> 5, lt = lane & 15;
 
     // kv head innermost: with H_kv a multiple of 8 every work-group of a kv
-    // head runs on one XCD and re-reads that group's Q and dO from its L2
+    // head runs on one XCD and re-reads that group's Q and dO from its L2.
+    // A split grid gives each of kv_split work-groups of a key tile
+    // group / kv_split consecutive query heads of the group.
     int id = blockIdx.x;
     const int hk = id % p.Hkv;
     id /= p.Hkv;
+    const int split = id % p.kv_split;
+    id /= p.kv_split;
+    const int gps = p.group / p.kv_split;  // query heads per work-group
+    const int h_first = hk * p.group + split * gps;
     const int b = id % p.B;
     id /= p.B;
     const int k0 = id * BK;  // causal: the first key tiles see the most queries (issued first)
@@ -357,10 +363,10 @@ bwd_dkdv_kernel(const BwdParams p)
     const int qt0 = CAUSAL ? min(k0, p.qL) / BQ : 0;
     const int n_qt = (p.qL + BQ - 1) / BQ;
     const int per_head = max(0, n_qt - qt0);
-    const int n_steps = (k0 < p.kL) ? per_head * p.group : 0;
+    const int n_steps = (k0 < p.kL) ? per_head * gps : 0;
 
     auto stage = [&](int step, int buf) __attribute__((always_inline)) {
-        const int h = hk * p.group + step / per_head;
+        const int h = h_first + step / per_head;
         const int q0 = (qt0 + step % per_head) * BQ;
         const int64_t qoff = (((int64_t)b * p.Hq + h) * p.qL) * D;
         bwd_stage_rows<D, TP, BQ, NW>((const uint16_t*)p.q + qoff, D, q0, p.qL, Qs[buf], wave, lane);
@@ -380,7 +386,7 @@ bwd_dkdv_kernel(const BwdParams p)
         bwd_wait_loads();
         __syncthreads();  // this step's tiles are in LDS; buffer buf ^ 1 is free
         if (step + 1 < n_steps) stage(step + 1, buf ^ 1);
-        const int h = hk * p.group + step / per_head;
+        const int h = h_first + step / per_head;
         const int q0 = (qt0 + step % per_head) * BQ;
         // a wave whose keys all follow the tile's last row skips it
         if (wk0 >= p.kL) continue;
@@ -465,6 +471,44 @@ bwd_dkdv_kernel(const BwdParams p)
             }
         }
     }
+    if (p.kv_split > 1) {
+        // fp32 partials of this work-group's heads.  A lane holds 4
+        // consecutive head-dim elements of its key per register quad; each
+        // wave passes its 32 keys through a 32 x 36 float region of the idle
+        // Q/dO buffers, one 32-column block at a time, so that every store
+        // writes whole 128-byte lines of four key rows.
+        constexpr int XP = 36, XE = 32 * XP * 2;  // region pitch (floats), size (16-bit elements)
+        constexpr int R = TT / XE;                // regions per buffer
+        static_assert(4 * R >= NW, "a partial region per wave");
+        __syncthreads();  // every wave is past its last read of the Q/dO buffers
+        const int w = wave;
+        float* xs = (float*)(w < R       ? &Qs[0][w * XE]
+                             : w < 2 * R ? &Qs[1][(w - R) * XE]
+                             : w < 3 * R ? &Os[0][(w - 2 * R) * XE]
+                                         : &Os[1][(w - 3 * R) * XE]);
+        const int64_t plane = (int64_t)p.B * p.Hkv * p.kL * D;  // one partial dK or dV
+        float* base = p.kv_part + 2 * (int64_t)split * plane + kvoff + (int64_t)wk0 * D;
+#pragma unroll
+        for (int which = 0; which < 2; ++which)
+#pragma unroll
+            for (int d = 0; d < ND; ++d) {
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const bwd_f32x16& a = which == 0 ? dk[d] : dv[d];
+                    *(bwd_f32x4*)(xs + r32 * XP + 8 * rq + 4 * g) =
+                        bwd_f32x4{a[4 * rq], a[4 * rq + 1], a[4 * rq + 2], a[4 * rq + 3]};
+                }
+                // lane l reads columns 4 (l % 8) .. +3 of key rows 8 i + l / 8
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rr = 8 * i + (lane >> 3), c4 = 4 * (lane & 7);
+                    const bwd_f32x4 v = *(const bwd_f32x4*)(xs + rr * XP + c4);
+                    if (wk0 + rr < p.kL)
+                        *(bwd_f32x4*)(base + which * plane + (int64_t)rr * D + 32 * d + c4) = v;
+                }
+            }
+        return;
+    }
     // dK = scale dK^T, dV = dV^T: key row `key`, head-dim 32 d + 8 rq + 4 g + {0..3}
     if (key_in) {
         uint16_t* krow = (uint16_t*)p.dk + kvoff + (int64_t)key * D;
@@ -484,6 +528,42 @@ bwd_dkdv_kernel(const BwdParams p)
     }
 }
 
+// Sum of the kv_split partials of a split dK/dV grid: dK = scale sum_s dK_s,
+// dV = sum_s dV_s in bf16; each thread takes 4 consecutive elements of one
+// key row of both.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_dkdv_reduce_kernel(const BwdParams p)
+{
+    const int64_t plane = (int64_t)p.B * p.Hkv * p.kL * D;
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= plane) return;
+    bwd_f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < p.kv_split; ++s) {
+        sk += *(const bwd_f32x4*)(p.kv_part + 2 * (int64_t)s * plane + e);
+        sv += *(const bwd_f32x4*)(p.kv_part + (2 * (int64_t)s + 1) * plane + e);
+    }
+    bwd_u32x2 wk, wv;
+    wk[0] = bwd_pack_bf16x2(sk[0] * p.scale, sk[1] * p.scale);
+    wk[1] = bwd_pack_bf16x2(sk[2] * p.scale, sk[3] * p.scale);
+    wv[0] = bwd_pack_bf16x2(sv[0], sv[1]);
+    wv[1] = bwd_pack_bf16x2(sv[2], sv[3]);
+    *(bwd_u32x2*)((uint16_t*)p.dk + e) = wk;
+    *(bwd_u32x2*)((uint16_t*)p.dv + e) = wv;
+}
+
+// Heads of a GQA group per dK/dV work-group: a grid with fewer work-groups
+// than CUs splits each group's query heads over up to 512 / work-groups of
+// them (a divisor of the group size).
+inline int bwd_kv_split(int64_t kv_wgs, int group)
+{
+    constexpr int kCUs = 256, kMaxWgs = 512;
+    if (kv_wgs <= 0 || kv_wgs >= kCUs) return 1;
+    int ns = 1;
+    for (int d = 2; d <= group; ++d)
+        if (group % d == 0 && kv_wgs * d <= kMaxWgs) ns = d;
+    return ns;
+}
+
 // Launch shapes: work-group waves and tile rows of the dQ and dK/dV grids.
 template <int D, int MASK, bool CAUSAL, int QNW, int BN, int QWPE, int KNW, int BQ, int KWPE>
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t st)
@@ -498,8 +578,34 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t st)
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t kv_wgs = (int64_t)((p.kL + KNW * 32 - 1) / (KNW * 32)) * p.Hkv * p.B;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK, CAUSAL, KNW, BQ, KWPE>), dim3((unsigned)kv_wgs), dim3(KNW * 64), 0, st, p);
-    return hipGetLastError();
+    BwdParams q = p;
+    q.kv_split = bwd_kv_split(kv_wgs, p.group);
+    q.kv_part = nullptr;
+    if (q.kv_split == 1) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK, CAUSAL, KNW, BQ, KWPE>), dim3((unsigned)kv_wgs), dim3(KNW * 64), 0,
+                           st, q);
+        return hipGetLastError();
+    }
+    // the partials come from the library's stream-ordered pool and go back
+    // to it once the reduction has read them; every partial element the
+    // reduction reads is written by the split grid first
+    const int64_t plane = (int64_t)p.B * p.Hkv * p.kL * D;
+    hipMemPool_t pool;
+    err = library_pool(&pool);
+    if (err != hipSuccess) return err;
+    void* ws = nullptr;
+    err = hipMallocFromPoolAsync(&ws, (size_t)(2 * q.kv_split * plane) * sizeof(float), pool, st);
+    if (err != hipSuccess) return err;
+    q.kv_part = (float*)ws;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK, CAUSAL, KNW, BQ, KWPE>), dim3((unsigned)(kv_wgs * q.kv_split)),
+                       dim3(KNW * 64), 0, st, q);
+    err = hipGetLastError();
+    if (err == hipSuccess) {
+        hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<D>), dim3((unsigned)((plane / 4 + 255) / 256)), dim3(256), 0, st, q);
+        err = hipGetLastError();
+    }
+    const hipError_t ferr = hipFreeAsync(ws, st);
+    return err != hipSuccess ? err : ferr;
 }
 
 }  // namespace

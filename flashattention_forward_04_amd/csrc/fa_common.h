@@ -82,6 +82,12 @@ struct BwdParams {
     float scale;        // natural-domain score scale (signed)
     float scale_log2;   // scale * log2(e)
     int mask_vec;       // mask rows admit 4-element vector loads
+    // dK/dV grid split over the heads of each GQA group (set by the
+    // launcher): kv_split work-groups per key tile, each over group /
+    // kv_split query heads, writing fp32 partials [s][dK, dV][B][H_kv][kL][D]
+    // that a reduction sums
+    float* kv_part;
+    int kv_split;
 };
 
 // Work-groups are dispatched round-robin over the 8 XCDs (each with its own

@@ -27,15 +27,16 @@
  *   - The call enqueues work on `hip_stream` (a hipStream_t; NULL = the null
  *     stream) and returns without synchronising.
  *   - Allocation: the forward path allocates no device memory, with one
- *     stated exception.  A bf16 call whose grid of query tiles leaves most
- *     CUs idle while its key range is long splits that range over
- *     work-groups, and takes fp32 partials (n_split * B * H_q * qL * (D + 1)
- *     * 4 bytes) from a stream-ordered memory pool that the library creates
- *     for itself on each device (hipMemPoolCreate; it keeps up to 256 MiB of
- *     freed memory for reuse).  They are returned to that pool on
+ *     stated exception.  A call (bf16 or fp32) whose grid of query tiles
+ *     leaves most CUs idle while its key range is long splits that range
+ *     over work-groups, and takes fp32 partials (n_split * B * H_q * qL *
+ *     (D + 1) * 4 bytes) from a stream-ordered memory pool that the library
+ *     creates for itself on each device (hipMemPoolCreate; it keeps up to
+ *     256 MiB of freed memory for reuse).  They are returned to that pool on
  *     `hip_stream` after the merge.  The device's default pool and every
  *     other process-wide allocator setting are left untouched.  Callers that
- *     cannot allocate use fa_fwd_strided_noalloc.
+ *     cannot allocate use fa_fwd_strided_noalloc.  fa_bwd takes the partials
+ *     of a split dK/dV grid from the same pool (see fa_bwd).
  *   - All argument checks run before any launch: a failed check writes
  *     nothing, launches nothing and returns FA_ERR_INVALID_ARGUMENT (or
  *     FA_ERR_UNSUPPORTED for a valid combination that is not built), with a
@@ -221,7 +222,13 @@ fa_status fa_fwd_window(const void* Q, const void* K, const void* V, const void*
  * All tensors are contiguous head-major.  Built for bf16 at D = 64 and 128,
  * every mask kind, causal or not; other valid combinations return
  * FA_ERR_UNSUPPORTED.  Three launches on `hip_stream` (Delta, then dQ, then
- * dK and dV); no atomics, so the result is deterministic; nothing is
+ * dK and dV); no atomics, so the result is deterministic.  When the dK/dV
+ * grid would leave CUs idle (fewer than 256 work-groups of 128 keys, e.g.
+ * B = 2, H_kv = 4, kL = 2048) and H_q / H_kv > 1, each GQA group's query
+ * heads are split over up to 512 / work-groups of them; their fp32 partial
+ * dK and dV (2 * split * B * H_kv * kL * D * 4 bytes, at most ~67 MB) come
+ * from the library's stream-ordered pool (as fa_fwd's split partials) and
+ * are summed, in a fixed order, by a fourth launch.  Otherwise nothing is
  * allocated.  Checks as fa_fwd, plus dO, Delta, dQ, dK, dV non-NULL and
  * aligned (16 bytes; 4 for L and Delta).
  */
