@@ -300,7 +300,9 @@ bwd_dq_kernel(const BwdParams p)
 }
 
 // ---------------------------------------------------------------- dK, dV
-template <int D, int MASK, bool CAUSAL, int NW, int BQ, int WPE>
+// KVS: the grid is split over each group's heads (fp32 partials); the
+// unsplit kernel is a separate instantiation so that its code is unchanged.
+template <int D, int MASK, bool CAUSAL, int NW, int BQ, int WPE, bool KVS>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 bwd_dkdv_kernel(const BwdParams p)
 {
@@ -327,9 +329,10 @@ bwd_dkdv_kernel(const BwdParams p)
     int id = blockIdx.x;
     const int hk = id % p.Hkv;
     id /= p.Hkv;
-    const int split = id % p.kv_split;
-    id /= p.kv_split;
-    const int gps = p.group / p.kv_split;  // query heads per work-group
+    const int kvs = KVS ? p.kv_split : 1;
+    const int split = id % kvs;
+    id /= kvs;
+    const int gps = p.group / kvs;  // query heads per work-group
     const int h_first = hk * p.group + split * gps;
     const int b = id % p.B;
     id /= p.B;
@@ -471,7 +474,7 @@ bwd_dkdv_kernel(const BwdParams p)
             }
         }
     }
-    if (p.kv_split > 1) {
+    if constexpr (KVS) {
         // fp32 partials of this work-group's heads.  A lane holds 4
         // consecutive head-dim elements of its key per register quad; each
         // wave passes its 32 keys through a 32 x 36 float region of the idle
@@ -582,8 +585,8 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t st)
     q.kv_split = bwd_kv_split(kv_wgs, p.group);
     q.kv_part = nullptr;
     if (q.kv_split == 1) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK, CAUSAL, KNW, BQ, KWPE>), dim3((unsigned)kv_wgs), dim3(KNW * 64), 0,
-                           st, q);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK, CAUSAL, KNW, BQ, KWPE, false>), dim3((unsigned)kv_wgs),
+                           dim3(KNW * 64), 0, st, q);
         return hipGetLastError();
     }
     // the partials come from the library's stream-ordered pool and go back
@@ -597,7 +600,7 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t st)
     err = hipMallocFromPoolAsync(&ws, (size_t)(2 * q.kv_split * plane) * sizeof(float), pool, st);
     if (err != hipSuccess) return err;
     q.kv_part = (float*)ws;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK, CAUSAL, KNW, BQ, KWPE>), dim3((unsigned)(kv_wgs * q.kv_split)),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK, CAUSAL, KNW, BQ, KWPE, true>), dim3((unsigned)(kv_wgs * q.kv_split)),
                        dim3(KNW * 64), 0, st, q);
     err = hipGetLastError();
     if (err == hipSuccess) {
