@@ -41,7 +41,12 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
-template <int D, int MASK, bool CAUSAL, int NW, int BN, bool DROP = false>
+// PACK (query ranges of at most 16 rows, GQA groups of a multiple of 4
+// heads): a wave's 32 rows are 16 rows each of two query heads of one group
+// (lane rows 0-15 the first, 16-31 the second), and a work-group takes 2 NW
+// heads of the group, so every matrix row is a real row and the work-group's
+// K/V tiles serve all of its heads.
+template <int D, int MASK, bool CAUSAL, int NW, int BN, bool DROP = false, bool PACK = false>
 __global__ void __launch_bounds__(NW * 64)
 fwd_f32_kernel(const FwdParams p)
 {
@@ -74,19 +79,39 @@ fwd_f32_kernel(const FwdParams p)
     const int g = lane >> 5;
 
     int id = blockIdx.x;
-    const int h = head_of(id % p.Hq, p.Hq);
-    id /= p.Hq;
-    // key range split over work-groups (n_split > 1): this work-group takes
-    // key tiles [split * split_tiles, (split + 1) * split_tiles)
-    const int split = id % p.n_split;
-    id /= p.n_split;
-    const int b = id % p.B;
-    id /= p.B;
-    const int qt = CAUSAL ? causal_tile(id, p.n_qtiles, p.pair_tiles) : id;
-    const int q0 = qt * BM;
-    const int hk = h / p.group;
-    const int wq0 = q0 + wave * 32;
-    const int qrow = wq0 + r32;
+    int h, hk, split, b, q0, wq0, qrow;
+    if constexpr (PACK) {
+        // kv head innermost (a group's work-groups on one XCD when H_kv is a
+        // multiple of 8), then the group's chunk of 2 NW heads, then the split
+        const int nch = p.group / (2 * NW);
+        hk = id % p.Hkv;
+        id /= p.Hkv;
+        const int c = id % nch;
+        id /= nch;
+        split = id % p.n_split;
+        id /= p.n_split;
+        b = id % p.B;
+        h = hk * p.group + c * 2 * NW + 2 * wave + (r32 >> 4);  // this lane's head
+        q0 = 0;
+        wq0 = 0;
+        qrow = r32 & 15;
+    } else {
+        h = head_of(id % p.Hq, p.Hq);
+        id /= p.Hq;
+        // key range split over work-groups (n_split > 1): this work-group takes
+        // key tiles [split * split_tiles, (split + 1) * split_tiles)
+        split = id % p.n_split;
+        id /= p.n_split;
+        b = id % p.B;
+        id /= p.B;
+        const int qt = CAUSAL ? causal_tile(id, p.n_qtiles, p.pair_tiles) : id;
+        q0 = qt * BM;
+        hk = h / p.group;
+        wq0 = q0 + wave * 32;
+        qrow = wq0 + r32;
+    }
+    // the last row any lane of this wave holds
+    const int wq_last = PACK ? 15 : wq0 + 31;
 
     const float* Qb = (const float*)p.q + b * p.q_s[0] + h * p.q_s[1];
     const float* Kb = (const float*)p.k + b * p.k_s[0] + hk * p.k_s[1];
@@ -106,7 +131,7 @@ fwd_f32_kernel(const FwdParams p)
     const int64_t drow = DROP ? (((int64_t)b * p.Hq + h) * p.qL + qrow) * p.kL : 0;
 
     const float c2 = p.scale_log2;
-    const int kv_end = CAUSAL ? min(p.kL, min(p.qL, q0 + BM)) : p.kL;
+    const int kv_end = CAUSAL ? min(p.kL, min(p.qL, PACK ? 16 : q0 + BM)) : p.kL;
     // causal sliding window: rows see keys from i - window + 1 on, so the
     // work-group starts at the tile of its first row's first key
     const bool win = CAUSAL && p.window > 0;
@@ -143,7 +168,7 @@ fwd_f32_kernel(const FwdParams p)
         }
 
         // (a tile reaching below the window of the wave's last row is masked too)
-        const bool w_edge = win && j0 < wq0 + 32 - p.window;
+        const bool w_edge = win && j0 < wq_last + 1 - p.window;
         const bool fast = (MASK == MASK_NONE) && (j0 + BN <= p.kL) && (!CAUSAL || j0 + BN - 1 <= wq0) && !w_edge;
         float cs = c2;
         if (!fast) {
@@ -247,7 +272,7 @@ fwd_f32_kernel(const FwdParams p)
     const int n_tiles = p.n_split > 1 ? min(n_all, t_first + p.split_tiles) : n_all;
     // this wave needs tiles 0..t_last (causal rows never see later keys)
     int t_last = n_tiles - 1;
-    if (CAUSAL) t_last = min(t_last, (wq0 + 31) / BN);
+    if (CAUSAL) t_last = min(t_last, wq_last / BN);
     if (wq0 >= p.qL) t_last = -1;  // every row of this wave is past qL: it only helps stage tiles
 
     // K tile t -> LDS directly: 1 KiB block i by wave i % NW, lane l writing
@@ -422,7 +447,7 @@ __global__ void __launch_bounds__(256) merge_splits_f32_kernel(const FwdParams p
 // one full GPU of work-groups, at least kMinSplitTiles tiles each (a multiple
 // of 2, the K ring depth).
 template <bool CAUSAL, int BN>
-int split_plan_f32(const FwdParams& p, int64_t wgs, int* split_tiles)
+int split_plan_f32(const FwdParams& p, int64_t wgs, int* split_tiles, int wgs_per_cu = 1)
 {
     constexpr int kCUs = 256;
     constexpr int kMinSplitTiles = 8;
@@ -430,7 +455,7 @@ int split_plan_f32(const FwdParams& p, int64_t wgs, int* split_tiles)
     const int n_kt = (kv_max + BN - 1) / BN;
     *split_tiles = 0;
     if (p.window > 0 || wgs * 2 > kCUs || n_kt < 2 * kMinSplitTiles) return 1;
-    const int64_t want = (int64_t)kCUs / wgs;  // one work-group per CU
+    const int64_t want = (int64_t)kCUs * wgs_per_cu / wgs;  // wgs_per_cu work-groups per CU
     const int by_len = n_kt / kMinSplitTiles;
     const int s0 = (int)(want < by_len ? want : (int64_t)by_len);
     if (s0 < 2) return 1;
@@ -440,15 +465,17 @@ int split_plan_f32(const FwdParams& p, int64_t wgs, int* split_tiles)
     return (n_kt + st - 1) / st;
 }
 
-template <int D, int MASK, bool CAUSAL, int NW, int BN, bool DROP = false>
+template <int D, int MASK, bool CAUSAL, int NW, int BN, bool DROP = false, bool PACK = false>
 hipError_t launch_f32(const FwdParams& p, hipStream_t st, size_t* need = nullptr)
 {
     // the kernel divides its grid index by n_split
     if (p.n_split < 1) return hipErrorInvalidValue;
     FwdParams q = p;
-    const int64_t wgs = (int64_t)p.n_qtiles * p.Hq * p.B;
+    // (packed: one work-group per 2 NW heads of a group, all query rows)
+    const int64_t wgs = PACK ? (int64_t)p.B * p.Hkv * (p.group / (2 * NW)) : (int64_t)p.n_qtiles * p.Hq * p.B;
     int split_tiles = 0;
-    const int n_split = split_plan_f32<CAUSAL, BN>(p, wgs, &split_tiles);
+    // (the packed shape fits two work-groups per CU)
+    const int n_split = split_plan_f32<CAUSAL, BN>(p, wgs, &split_tiles, PACK ? 2 : 1);
     const int64_t rows = (int64_t)p.B * p.Hq * p.qL;
     const size_t ws_bytes = n_split < 2 ? 0 : (size_t)n_split * rows * (D + 1) * sizeof(float);
     if (need) {
@@ -457,8 +484,8 @@ hipError_t launch_f32(const FwdParams& p, hipStream_t st, size_t* need = nullptr
     }
     if (n_split < 2) {
         q.pair_tiles = CAUSAL && grid_fits_at_once(wgs, 1);
-        hipLaunchKernelGGL((fwd_f32_kernel<D, MASK, CAUSAL, NW, BN, DROP>), dim3((unsigned)wgs), dim3(NW * 64), 0, st,
-                           q);
+        hipLaunchKernelGGL((fwd_f32_kernel<D, MASK, CAUSAL, NW, BN, DROP, PACK>), dim3((unsigned)wgs), dim3(NW * 64), 0,
+                           st, q);
         return hipGetLastError();
     }
     // partials in the caller's scratch or from the library's stream-ordered
@@ -480,7 +507,7 @@ hipError_t launch_f32(const FwdParams& p, hipStream_t st, size_t* need = nullptr
     q.n_split = n_split;
     q.split_tiles = split_tiles;
     q.pair_tiles = CAUSAL && grid_fits_at_once(wgs * n_split, 1);
-    hipLaunchKernelGGL((fwd_f32_kernel<D, MASK, CAUSAL, NW, BN, DROP>), dim3((unsigned)(wgs * n_split)),
+    hipLaunchKernelGGL((fwd_f32_kernel<D, MASK, CAUSAL, NW, BN, DROP, PACK>), dim3((unsigned)(wgs * n_split)),
                        dim3(NW * 64), 0, st, q);
     err = hipGetLastError();
     if (err == hipSuccess) {
@@ -492,10 +519,25 @@ hipError_t launch_f32(const FwdParams& p, hipStream_t st, size_t* need = nullptr
     return err != hipSuccess ? err : ferr;
 }
 
+// Query ranges of at most 16 rows in GQA groups of a multiple of 4 heads (a
+// decode step) take the packed shape: 2-wave work-groups of 4 heads x 16
+// rows with 32-key tiles (two work-groups per CU).  Everything else takes the
+// head dim's own shape.
+template <int D, int MASK, bool CAUSAL, int NW, int BN, bool DROP = false>
+hipError_t launch_f32_any(const FwdParams& p, hipStream_t st, size_t* need = nullptr)
+{
+    if (p.qL <= 16 && p.group % 4 == 0 && p.window == 0) {
+        FwdParams q = p;
+        q.n_qtiles = 1;
+        return launch_f32<D, MASK, CAUSAL, 2, 32, DROP, true>(q, st, need);
+    }
+    return launch_f32<D, MASK, CAUSAL, NW, BN, DROP>(p, st, need);
+}
+
 }  // namespace
 
 #define FA_F32_VARIANT(D, MASK, CAUSAL, NW, BN, NAME) \
-    {NAME, 0, D, MASK, CAUSAL, NW * 32, &launch_f32<D, MASK, CAUSAL, NW, BN>}
+    {NAME, 0, D, MASK, CAUSAL, NW * 32, &launch_f32_any<D, MASK, CAUSAL, NW, BN>}
 
 #define FA_F32_FOR_D(D, NW, BN)                                                         \
     FA_F32_VARIANT(D, MASK_NONE, false, NW, BN, "fwd_f32_d" #D "_nomask"),              \
@@ -537,7 +579,7 @@ hipError_t launch_f32(const FwdParams& p, hipStream_t st, size_t* need = nullptr
 // Dropout variants: the same kernel at the same launch shapes, with the
 // multipliers applied to the fp32 P before P V.
 #define FA_F32_DROP_VARIANT(D, MASK, CAUSAL, NW, BN, NAME) \
-    {NAME, 0, D, MASK, CAUSAL, NW * 32, &launch_f32<D, MASK, CAUSAL, NW, BN, true>}
+    {NAME, 0, D, MASK, CAUSAL, NW * 32, &launch_f32_any<D, MASK, CAUSAL, NW, BN, true>}
 #define FA_F32_DROP_FOR_D(D, NW, BN)                                                           \
     FA_F32_DROP_VARIANT(D, MASK_NONE, false, NW, BN, "fwd_f32_d" #D "_nomask_dropout"),        \
     FA_F32_DROP_VARIANT(D, MASK_NONE, true, NW, BN, "fwd_f32_d" #D "_nomask_causal_dropout"),  \

@@ -420,6 +420,41 @@ def test_key_range_split_over_work_groups_f32(B, Hq, Hkv, qL, kL, D, kind, causa
         assert np.all(O[0, Hq - 1, qL // 2] == 0) and L[0, Hq - 1, qL // 2] == 0
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,qL,kL,D,kind,causal", [
+    (1, 8, 2, 1, 300, 64, "none", False),
+    (2, 16, 2, 7, 5000, 128, "additive", False),
+    (1, 8, 2, 16, 2048, 128, "bool", True),
+    (1, 4, 1, 3, 777, 16, "none", False),
+    (1, 12, 3, 16, 4096, 80, "additive", False),
+    (1, 8, 2, 16, 4096, 256, "none", False),
+    (1, 4, 1, 16, 9000, 128, "bool", False),
+], ids=lambda x: str(x))
+def test_packed_short_queries_f32(B, Hq, Hkv, qL, kL, D, kind, causal):
+    """The fp32 kernel's packed shape (at most 16 query rows, GQA groups of a
+    multiple of 4): a wave holds 16 rows of each of two heads, a work-group
+    four heads of one group; split and unsplit key ranges, every mask kind,
+    causal, and a row with no allowed key."""
+    print(f"[case] f32 packed B={B} Hq={Hq} Hkv={Hkv} qL={qL} kL={kL} D={D} mask={kind} causal={causal}", flush=True)
+    q, k, v = _rand((B, Hq, qL, D), F32, 55), _rand((B, Hkv, kL, D), F32, 56), _rand((B, Hkv, kL, D), F32, 57)
+    mask = None
+    if kind != "none":
+        rng = np.random.default_rng(58)
+        masked = W.draw_masked(rng, (B, Hq, qL, kL), 0.3)
+        masked[0, Hq - 1, qL // 2, :] = True  # no allowed key
+        if kind == "bool":
+            mask = torch.from_numpy((~masked).astype(np.uint8))
+        else:
+            m = rng.standard_normal(masked.shape).astype(np.float32)
+            m[masked] = -np.inf
+            mask = torch.from_numpy(m)
+    scale = 1 / math.sqrt(D)
+    O, L, _ = run_gpu(q, k, v, mask, causal=causal, scale=scale)
+    Oref, Lref = run_oracle(q, k, v, mask, causal=causal, scale=scale)
+    assert_parity(O, L, Oref, Lref, "f32", f"f32 packed qL={qL} kL={kL} D={D} {kind} causal={causal}")
+    if kind != "none":
+        assert np.all(O[0, Hq - 1, qL // 2] == 0) and L[0, Hq - 1, qL // 2] == 0
+
+
 @pytest.mark.parametrize("Hq,Hkv,qL,kL,D,kind,causal", [
     (8, 4, 1, 4096, 128, "none", False),
     (8, 2, 17, 3000, 128, "additive", False),
