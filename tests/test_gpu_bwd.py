@@ -110,6 +110,15 @@ def test_shapes(D, causal, qL, kL):
 
 
 @pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv,kind,causal", [(16, 2, "none", False), (16, 2, "bool", True), (24, 4, "additive", False),
+                                               (8, 8, "none", True)], ids=lambda x: str(x))
+def test_group_splits(D, Hq, Hkv, kind, causal):
+    """Small dK/dV grids split over each group's heads in 8 (group 8), 6
+    (group 6) and 1 (MHA) ways; the partials are summed in a fixed order."""
+    _case(1, Hq, Hkv, 200, 333, D, causal, 650 + D + Hq, mask_kind=kind, empty_row=kind != "none")
+
+
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("kind", ["additive", "bool"])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 def test_masks(D, kind, causal):
