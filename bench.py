@@ -49,7 +49,7 @@ def kernel_sources(w) -> list:
     if w.backward:
         return common + ["fa_bwd_bf16.h", f"fa_bwd_bf16_d{w.D}.hip"]
     kind = "bf16" if w.dtype == "bf16" else "f32"
-    return common + [f"fa_fwd_{kind}.h", f"fa_fwd_{kind}_d{w.D}.hip"]
+    return common + [f"fa_fwd_{kind}.h", "fa_merge.h", f"fa_fwd_{kind}_d{w.D}.hip"]
 
 
 def kernel_source_hash(w) -> str:

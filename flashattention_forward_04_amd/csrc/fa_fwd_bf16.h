@@ -52,6 +52,7 @@
 #pragma once
 
 #include "fa_common.h"
+#include "fa_merge.h"
 
 #include <math.h>
 
@@ -167,8 +168,13 @@ __device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
 // so a long causal row block takes half as many steps.  At the end the two
 // softmax states (m, l, O) of each row are merged through LDS -- the same
 // combination the online softmax applies between key blocks.
+//
+// RPACK (query ranges of at most 16 rows, GQA groups of a multiple of 2 NW
+// heads): a wave's 32 rows are 16 rows each of two query heads of one group
+// (lanes with row bit 4 clear the first, set the second), and the work-group
+// takes 2 NW heads of the group; every matrix row is then a real row.
 template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB, bool DROP = false,
-          bool KSPLIT = false>
+          bool KSPLIT = false, bool RPACK = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fwd_bf16_kernel(const FwdParams p)
 {
@@ -252,7 +258,20 @@ fwd_bf16_kernel(const FwdParams p)
     int id = blockIdx.x;
     int h, hk, split, b, q0, wq0;
     bool head_ok = true;  // false: a packed wave past the end of its group
-    if (p.head_pack) {
+    if constexpr (RPACK) {
+        // kv head innermost, then the group's chunk of 2 NW heads, then the split
+        const int nch = p.group / (2 * NW);
+        hk = id % p.Hkv;
+        id /= p.Hkv;
+        const int c = id % nch;
+        id /= nch;
+        split = id % p.n_split;
+        id /= p.n_split;
+        b = id % p.B;
+        h = hk * p.group + c * 2 * NW + 2 * wave + (r32 >> 4);  // this lane's head
+        q0 = 0;
+        wq0 = 0;
+    } else if (p.head_pack) {
         // kv head innermost: the work-groups of one kv head's group sit H_kv
         // ids apart, on one XCD (one L2) when H_kv is a multiple of 8
         const int nch = (p.group + NW - 1) / NW;
@@ -281,7 +300,8 @@ fwd_bf16_kernel(const FwdParams p)
         hk = h / p.group;
         wq0 = q0 + wrow * 32;  // first query row of this wave
     }
-    const int qrow = wq0 + r32;  // this lane's query row
+    const int qrow = RPACK ? (r32 & 15) : wq0 + r32;  // this lane's query row
+    const int wq_last = RPACK ? 15 : wq0 + 31;         // the last row any lane of this wave holds
 
     const uint16_t* Qb = (const uint16_t*)p.q + b * p.q_s[0] + h * p.q_s[1];
     const uint16_t* Kb = (const uint16_t*)p.k + b * p.k_s[0] + hk * p.k_s[1];
@@ -302,7 +322,7 @@ fwd_bf16_kernel(const FwdParams p)
     }
 
     const float c2 = p.scale_log2;
-    const int kv_end = CAUSAL ? min(p.kL, min(p.qL, q0 + (p.head_pack ? 32 : BM))) : p.kL;
+    const int kv_end = CAUSAL ? min(p.kL, min(p.qL, q0 + (RPACK ? 16 : p.head_pack ? 32 : BM))) : p.kL;
     // key tiles of this query tile; a split work-group takes tiles
     // [tb, tb + split_tiles) of them, numbered from 0 below.  A sliding
     // window starts the range at the tile of the first row's first key.
@@ -318,7 +338,7 @@ fwd_bf16_kernel(const FwdParams p)
     const int n_steps = nh;                                            // loop steps of the work-group
     // this wave needs tiles 0..t_last (a prefix: causal rows never see later keys)
     int t_last = n_tiles - 1;
-    if (CAUSAL) t_last = min(t_last, (wq0 + 31) / BN - tb);
+    if (CAUSAL) t_last = min(t_last, wq_last / BN - tb);
     if (wq0 >= p.qL || !head_ok) t_last = -1;
 
     // dropout: the score position of this lane's row at key 0, and the
@@ -828,7 +848,9 @@ fwd_bf16_kernel(const FwdParams p)
                                  : w < 2 * RK       ? Ks1 + (w - RK) * XE
                                  : w < 2 * RK + RV  ? Vs0 + (w - 2 * RK) * XE
                                                     : Vs1 + (w - 2 * RK - RV) * XE);
-            const int64_t row0 = ((int64_t)b * p.Hq + h) * p.qL + wq0;  // this wave's first row
+            // this wave's first row (RPACK: of the wave's first head; its
+            // second head's rows start 16 region rows later)
+            const int64_t row0 = ((int64_t)b * p.Hq + (RPACK ? hk * p.group + (h - hk * p.group) / 2 * 2 : h)) * p.qL + wq0;
 #pragma unroll
             for (int d = 0; d < ND; ++d) {
 #pragma unroll
@@ -840,8 +862,11 @@ fwd_bf16_kernel(const FwdParams p)
                 for (int i = 0; i < 4; ++i) {
                     const int rr = 8 * i + (lane >> 3), c4 = 4 * (lane & 7);
                     const f32x4 v = *(const f32x4*)(xs + rr * XP + c4);
-                    if (32 * d + c4 < D && wq0 + rr < p.qL && head_ok)
-                        *(f32x4*)(p.o_part + ((int64_t)split * rows + row0 + rr) * D + 32 * d + c4) = v;
+                    // (RPACK: region row rr is row rr % 16 of the wave's head rr / 16)
+                    const int rq_ = RPACK ? (rr & 15) : wq0 + rr;
+                    const int64_t ri = RPACK ? row0 + (int64_t)(rr >> 4) * p.qL + (rr & 15) : row0 + rr;
+                    if (32 * d + c4 < D && rq_ < p.qL && head_ok)
+                        *(f32x4*)(p.o_part + ((int64_t)split * rows + ri) * D + 32 * d + c4) = v;
                 }
             }
         } else if (row_ok) {
@@ -879,57 +904,6 @@ fwd_bf16_kernel(const FwdParams p)
     }
 }
 
-// Merge of a split launch (one wave per query row): with L_s the natural-log
-// L of key range s, L = ln sum_s e^{L_s} and O = sum_s e^{L_s - L} O_s -- the
-// same combination the online softmax applies between key blocks, here on
-// normalised partials.  Ranges with no allowed key (L_s = -inf) weigh 0; a
-// row with none at all gets O = 0, L = 0.
-template <int D>
-__global__ void __launch_bounds__(256) merge_splits_bf16_kernel(const FwdParams p)
-{
-    constexpr int NE = (D + 63) / 64;  // head-dim elements per lane
-    const int lane = threadIdx.x & 63;
-    const int64_t rows = (int64_t)p.B * p.Hq * p.qL;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
-    const int i = (int)(row % p.qL);
-    const int64_t bh = row / p.qL;
-    const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
-    // the largest L_s and sum_s e^{L_s - max}: the splits spread over the
-    // lanes, then reduced across the wave
-    float lmax = -INFINITY;
-    for (int s = lane; s < p.n_split; s += 64) lmax = fmaxf(lmax, p.l_part[s * rows + row]);
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, m));
-    float acc[NE];
-#pragma unroll
-    for (int e = 0; e < NE; ++e) acc[e] = 0.f;
-    float sum = 0.f;
-    if (lmax != -INFINITY) {
-        for (int s = lane; s < p.n_split; s += 64)
-            sum += __builtin_amdgcn_exp2f((p.l_part[s * rows + row] - lmax) * kLog2e);
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
-        // O = sum_s e^{L_s - max} O_s / sum; an empty range has L_s = -inf
-        // and weighs exactly 0.  Unrolled so that the partial rows of several
-        // splits are in flight together.
-#pragma unroll 8
-        for (int s = 0; s < p.n_split; ++s) {
-            const float w = __builtin_amdgcn_exp2f((p.l_part[s * rows + row] - lmax) * kLog2e);
-            const float* src = p.o_part + (s * rows + row) * D;
-#pragma unroll
-            for (int e = 0; e < NE; ++e)
-                if (lane + 64 * e < D) acc[e] = __builtin_fmaf(w, src[lane + 64 * e], acc[e]);
-        }
-    }
-    const float inv = (sum > 0.f) ? 1.f / sum : 0.f;
-    uint16_t* orow = (uint16_t*)p.o + b * p.o_s[0] + h * p.o_s[1] + (int64_t)i * p.o_s[2];
-#pragma unroll
-    for (int e = 0; e < NE; ++e)
-        if (lane + 64 * e < D) orow[lane + 64 * e] = (uint16_t)(pack_bf16x2(acc[e] * inv, 0.f) & 0xffffu);
-    if (lane == 0) p.lse[row] = (sum > 0.f) ? lmax + __builtin_amdgcn_logf(sum) * kLn2 : 0.f;
-}
-
 // Work-groups of the work-group kernel one CU holds: by waves per SIMD, and
 // by LDS (tiles padded to 1 KiB blocks, NB buffers each for K and V).
 template <int D, int NW, int BN, int WPE, int NB>
@@ -964,7 +938,7 @@ int split_plan(const FwdParams& p, int64_t wgs, int wgs_per_cu_, int* split_tile
 }
 
 template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB, bool DROP = false,
-          bool KSPLIT = false>
+          bool KSPLIT = false, bool RPACK = false>
 hipError_t launch_bf16(const FwdParams& p, hipStream_t st, size_t* need = nullptr)
 {
     // the work-group kernel divides its grid index by n_split
@@ -972,8 +946,9 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t st, size_t* need = nullpt
     // (key halves: twice the LDS ring, and never a split over work-groups)
     constexpr int kWgsPerCu = wgs_per_cu<D, NW, BN, WPE, KSPLIT ? 2 * NB : NB>();
     FwdParams q = p;
-    const int64_t wgs = p.head_pack ? (int64_t)p.n_qtiles * ((p.group + NW - 1) / NW) * p.Hkv * p.B
-                                    : (int64_t)p.n_qtiles * p.Hq * p.B;
+    const int64_t wgs = RPACK       ? (int64_t)p.B * p.Hkv * (p.group / (2 * NW))
+                        : p.head_pack ? (int64_t)p.n_qtiles * ((p.group + NW - 1) / NW) * p.Hkv * p.B
+                                      : (int64_t)p.n_qtiles * p.Hq * p.B;
     int split_tiles = 0;
     const int n_split = KSPLIT ? 1 : split_plan<CAUSAL, BN, NB>(p, wgs, kWgsPerCu, &split_tiles);
     const int64_t rows = (int64_t)p.B * p.Hq * p.qL;
@@ -984,7 +959,7 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t st, size_t* need = nullpt
     }
     if (n_split < 2) {
         q.pair_tiles = CAUSAL && grid_fits_at_once(wgs, kWgsPerCu);
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB, DROP, KSPLIT>),
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB, DROP, KSPLIT, RPACK>),
                            dim3((unsigned)wgs), dim3(NW * 64), 0, st, q);
         return hipGetLastError();
     }
@@ -1008,12 +983,11 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t st, size_t* need = nullpt
     q.n_split = n_split;
     q.split_tiles = split_tiles;
     q.pair_tiles = CAUSAL && grid_fits_at_once(wgs * n_split, kWgsPerCu);
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB, DROP, KSPLIT>),
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, CAUSAL, NW, BN, WPE, SCHED, NB, DROP, KSPLIT, RPACK>),
                        dim3((unsigned)(wgs * n_split)), dim3(NW * 64), 0, st, q);
     err = hipGetLastError();
     if (err == hipSuccess) {
-        hipLaunchKernelGGL((merge_splits_bf16_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, q);
-        err = hipGetLastError();
+        err = launch_merge<D, true>(q, rows, st);
     }
     if (p.ws != nullptr) return err;
     const hipError_t ferr = hipFreeAsync(ws, st);
@@ -1534,6 +1508,12 @@ fwd_bf16_stream_kernel(const FwdParams p, int wgs_per_head)
 constexpr int kShortKeys = 256;
 // Query ranges up to this many rows take 2-wave work-groups.
 constexpr int kShortQueries = 64;
+// Waves per work-group, keys per tile, waves per SIMD, schedule and ring
+// depth of the packed short-query shape (by default 2-wave work-groups with
+// the head dim's main tile shape).
+#ifndef FA_BF16_RPACK_SHAPE
+#define FA_BF16_RPACK_SHAPE 2, BN, WPE, SCHED, NB
+#endif
 template <int D, int MASK, bool CAUSAL, int NW, int BN, int WPE, int SCHED, int NB>
 hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st, size_t* need = nullptr)
 {
@@ -1564,6 +1544,11 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st, size_t* need = nu
         // fit per CU (the split plan then cuts a long key range finer).
         if (p.qL <= kShortQueries) {
             FwdParams q = p;
+            if (p.qL <= 16 && p.group % 4 == 0 && p.window == 0) {
+                // at most 16 rows: each wave holds two query heads' rows
+                q.n_qtiles = 1;
+                return launch_bf16<D, MASK, CAUSAL, FA_BF16_RPACK_SHAPE, false, false, true>(q, st, need);
+            }
             if (p.qL <= 32 && p.group >= 2) {
                 // one 32-row tile: pack two query heads of a GQA group
                 q.head_pack = 1;

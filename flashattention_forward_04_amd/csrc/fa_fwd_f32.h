@@ -26,6 +26,7 @@
 #pragma once
 
 #include "fa_common.h"
+#include "fa_merge.h"
 
 #include <math.h>
 
@@ -397,50 +398,6 @@ fwd_f32_kernel(const FwdParams p)
     }
 }
 
-// Merge of a split fp32 launch (one wave per query row): with L_s the
-// natural-log L of key range s, L = ln sum_s e^{L_s} and O = sum_s e^{L_s - L}
-// O_s, written through O's strides.  Ranges with no allowed key (L_s = -inf)
-// weigh 0; a row with none at all gets O = 0, L = 0.
-template <int D>
-__global__ void __launch_bounds__(256) merge_splits_f32_kernel(const FwdParams p)
-{
-    constexpr int NE = (D + 63) / 64;  // head-dim elements per lane
-    const int lane = threadIdx.x & 63;
-    const int64_t rows = (int64_t)p.B * p.Hq * p.qL;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
-    const int i = (int)(row % p.qL);
-    const int64_t bh = row / p.qL;
-    const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
-    float lmax = -INFINITY;
-    for (int s = lane; s < p.n_split; s += 64) lmax = fmaxf(lmax, p.l_part[s * rows + row]);
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, m));
-    float acc[NE];
-#pragma unroll
-    for (int e = 0; e < NE; ++e) acc[e] = 0.f;
-    float sum = 0.f;
-    if (lmax != -INFINITY) {
-        for (int s = lane; s < p.n_split; s += 64) sum += __builtin_amdgcn_exp2f((p.l_part[s * rows + row] - lmax) * kLog2e);
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
-#pragma unroll 8
-        for (int s = 0; s < p.n_split; ++s) {
-            const float w = __builtin_amdgcn_exp2f((p.l_part[s * rows + row] - lmax) * kLog2e);
-            const float* src = p.o_part + (s * rows + row) * D;
-#pragma unroll
-            for (int e = 0; e < NE; ++e)
-                if (lane + 64 * e < D) acc[e] = __builtin_fmaf(w, src[lane + 64 * e], acc[e]);
-        }
-    }
-    const float inv = (sum > 0.f) ? 1.f / sum : 0.f;
-    float* orow = (float*)p.o + b * p.o_s[0] + h * p.o_s[1] + (int64_t)i * p.o_s[2];
-#pragma unroll
-    for (int e = 0; e < NE; ++e)
-        if (lane + 64 * e < D) orow[lane + 64 * e] = acc[e] * inv;
-    if (lane == 0) p.lse[row] = (sum > 0.f) ? lmax + __builtin_amdgcn_logf(sum) * kLn2 : 0.f;
-}
-
 // How many work-groups a query tile's key range is split over (1: none): a
 // grid that leaves more than half of the CUs idle while each work-group walks
 // a long key range (at least 2 kMinSplitTiles tiles) splits that range, up to
@@ -511,8 +468,7 @@ hipError_t launch_f32(const FwdParams& p, hipStream_t st, size_t* need = nullptr
                        dim3(NW * 64), 0, st, q);
     err = hipGetLastError();
     if (err == hipSuccess) {
-        hipLaunchKernelGGL((merge_splits_f32_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, q);
-        err = hipGetLastError();
+        err = launch_merge<D, false>(q, rows, st);
     }
     if (p.ws != nullptr) return err;
     const hipError_t ferr = hipFreeAsync(ws, st);

@@ -455,6 +455,47 @@ def test_packed_short_queries_f32(B, Hq, Hkv, qL, kL, D, kind, causal):
         assert np.all(O[0, Hq - 1, qL // 2] == 0) and L[0, Hq - 1, qL // 2] == 0
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,qL,kL,D,kind,causal", [
+    (1, 8, 2, 1, 300, 64, "none", False),
+    (2, 16, 2, 7, 5000, 128, "additive", False),
+    (1, 8, 2, 16, 2048, 128, "bool", True),
+    (1, 4, 1, 3, 777, 16, "none", False),
+    (1, 8, 1, 11, 1500, 32, "bool", False),
+    (1, 4, 1, 16, 2100, 48, "additive", True),
+    (1, 12, 3, 16, 4096, 80, "additive", False),
+    (2, 8, 2, 9, 6000, 96, "none", False),
+    (1, 8, 2, 16, 4096, 256, "none", False),
+    (1, 8, 2, 5, 3001, 256, "bool", False),
+    (1, 4, 1, 16, 9000, 128, "bool", False),
+    (1, 32, 8, 16, 32768, 128, "none", False),
+], ids=lambda x: str(x))
+def test_packed_short_queries_bf16(B, Hq, Hkv, qL, kL, D, kind, causal):
+    """The bf16 kernel's packed shape (at most 16 query rows, GQA groups of a
+    multiple of 4): a wave holds 16 rows of each of two heads, a work-group
+    four heads of one group; split and unsplit key ranges, every mask kind,
+    causal, every head dimension, and a row with no allowed key."""
+    print(f"[case] bf16 packed B={B} Hq={Hq} Hkv={Hkv} qL={qL} kL={kL} D={D} mask={kind} causal={causal}",
+          flush=True)
+    q, k, v = _rand((B, Hq, qL, D), BF16, 65), _rand((B, Hkv, kL, D), BF16, 66), _rand((B, Hkv, kL, D), BF16, 67)
+    mask = None
+    if kind != "none":
+        rng = np.random.default_rng(68)
+        masked = W.draw_masked(rng, (B, Hq, qL, kL), 0.3)
+        masked[0, Hq - 1, qL // 2, :] = True  # no allowed key
+        if kind == "bool":
+            mask = torch.from_numpy((~masked).astype(np.uint8))
+        else:
+            m = rng.standard_normal(masked.shape).astype(np.float32)
+            m[masked] = -np.inf
+            mask = torch.from_numpy(m).to(BF16)
+    scale = 1 / math.sqrt(D)
+    O, L, _ = run_gpu(q, k, v, mask, causal=causal, scale=scale)
+    Oref, Lref = run_oracle(q, k, v, mask, causal=causal, scale=scale)
+    assert_parity(O, L, Oref, Lref, "bf16", f"bf16 packed qL={qL} kL={kL} D={D} {kind} causal={causal}")
+    if kind != "none":
+        assert np.all(O[0, Hq - 1, qL // 2] == 0) and L[0, Hq - 1, qL // 2] == 0
+
+
 @pytest.mark.parametrize("Hq,Hkv,qL,kL,D,kind,causal", [
     (8, 4, 1, 4096, 128, "none", False),
     (8, 2, 17, 3000, 128, "additive", False),
@@ -554,6 +595,28 @@ def test_split_over_more_ranges_than_lanes():
     O, L, _ = run_gpu(q, k, v, scale=1 / math.sqrt(128))
     Oref, Lref = run_oracle(q, k, v, scale=1 / math.sqrt(128))
     assert_parity(O, L, Oref, Lref, "bf16", "split into 128 ranges")
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("D", [16, 64, 128, 256])
+@pytest.mark.parametrize("kL", [2048, 4096, 8192, 16384, 40000])
+def test_split_merge_range_counts(kL, D, dtype):
+    """One head, one query tile: the number of key ranges grows with kL
+    (about kL / 512 up to the GPU's fill), so the merge runs with one, two
+    and four waves per row and with every lane layout of a partial row.  A
+    bool mask leaves one query row a single allowed key near the end and
+    another only keys of the first range, so most ranges weigh 0 there."""
+    print(f"[case] merge kL={kL} D={D} {dtype}", flush=True)
+    q, k, v = _rand((1, 1, 64, D), dtype, 91), _rand((1, 1, kL, D), dtype, 92), _rand((1, 1, kL, D), dtype, 93)
+    allow = np.ones((1, 1, 64, kL), dtype=np.uint8)
+    allow[0, 0, 5, :] = 0
+    allow[0, 0, 5, kL - 3] = 1
+    allow[0, 0, 9, 300:] = 0
+    mask = torch.from_numpy(allow)
+    scale = 1 / math.sqrt(D)
+    O, L, _ = run_gpu(q, k, v, mask, scale=scale)
+    Oref, Lref = run_oracle(q, k, v, mask, scale=scale)
+    assert_parity(O, L, Oref, Lref, "bf16" if dtype == BF16 else "f32", f"merge kL={kL} D={D}")
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,qL,kL,D,window,kind", [
