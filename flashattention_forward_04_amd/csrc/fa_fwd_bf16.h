@@ -410,19 +410,15 @@ fwd_bf16_kernel(const FwdParams p)
                     const uint16_t* src =
                         FULL ? (const uint16_t*)((const char*)tbase + off[k])
                              : gbase + (int64_t)min(j0 + row, p.kL - 1) * stride + ch * 8;
-                    if (MASK == MASK_NONE && FULL) {
+                    // (the compiler does not count these loads: a wait it
+                    // places for a later ordinary load, e.g. of mask words,
+                    // counts fewer loads in flight than there are, so it
+                    // waits longer, never shorter; the tiles themselves are
+                    // waited for explicitly at the end of each step)
+                    if (FULL)
                         lds_dma16_so(tbase, off[k], (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(lds + 512 * i));
-                    } else if (MASK == MASK_NONE) {
+                    else
                         lds_dma16(src, (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(lds + 512 * i));
-                    } else {
-                        // the masked kernels load the mask with ordinary
-                        // loads whose compiler waits would also wait for
-                        // untracked direct loads, so here the compiler
-                        // tracks them
-                        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                                         (__attribute__((address_space(3))) void*)(lds + 512 * i), 16,
-                                                         0, 0);
-                    }
                 }
             }
         };
@@ -532,6 +528,28 @@ fwd_bf16_kernel(const FwdParams p)
                     s[c][r] = (32 * c + 8 * (r >> 2) + (r & 3) <= lim) ? s[c][r] * c2 : -INFINITY;
             return;
         }
+        // the bias of element e of a quad: bf16 bits in the low or high half
+        // (a bias of -inf excludes the key by itself)
+        auto bias = [&](const u32x2& w, int e) __attribute__((always_inline)) {
+            return __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
+        };
+        // Tiles inside the key range, below the causal diagonal and the
+        // window's edge: only the user mask decides (wave-uniform branch)
+        if (j0 + BN <= p.kL && !(CAUSAL && j0 + BN - 1 > wq0) && !w_edge) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const u32x2 w = mw[c][rq];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = s[c][4 * rq + e];
+                        if (MASK == MASK_ADD) s[c][4 * rq + e] = __builtin_fmaf(bias(w, e), kLog2e, x * c2);
+                        if (MASK == MASK_BOOL) s[c][4 * rq + e] = ((w[0] >> (8 * e)) & 0xffu) != 0 ? x * c2 : -INFINITY;
+                    }
+                }
+            return;
+        }
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
 #pragma unroll
@@ -546,10 +564,7 @@ fwd_bf16_kernel(const FwdParams p)
                     if (CAUSAL) ok = ok && (j <= qrow);
                     if (CAUSAL) ok = ok && (!w_edge || j > qrow - p.window);
                     float x = s[c][4 * rq + e] * c2;
-                    if (MASK == MASK_ADD) {
-                        const uint32_t bits = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                        x = __builtin_fmaf(bf16_bits_to_float(bits), kLog2e, x);
-                    }
+                    if (MASK == MASK_ADD) x = __builtin_fmaf(bias(w, e), kLog2e, x);
                     s[c][4 * rq + e] = ok ? x : -INFINITY;
                 }
             }
