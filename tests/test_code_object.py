@@ -1,13 +1,14 @@
 """Checks on the built gfx950 code object (CPU only: it is disassembled, not run).
 
-The unmasked kernels (and the short-key streaming kernel) issue their
-direct global->LDS loads from inline assembly that sets M0 and leaves it
-set.  That is only sound while no instruction in those kernels relies on M0
-keeping a value across other code.  They are checked for that here: M0 is
-only ever written, and each instruction that reads it (the direct loads)
-follows its own M0 write, with at most one wait state in between.  (The
-masked kernels use the compiler's own direct-load builtin, whose M0 the
-compiler tracks; they are not checked.)
+The bf16 work-group kernels (every mask kind), the unmasked fp32 kernels
+and the short-key streaming kernel issue their direct global->LDS loads from
+inline assembly that sets M0 and leaves it set.  That is only sound while no
+instruction in those kernels relies on M0 keeping a value across other code.
+They are checked for that here: M0 is only ever written, and each
+instruction that reads it (the direct loads) follows its own M0 write, with
+at most one wait state in between.  (The masked fp32 kernels use the
+compiler's own direct-load builtin, whose M0 the compiler tracks; they are
+not checked.)
 """
 import os
 import re
@@ -78,9 +79,9 @@ def _operands(ins):
     return parts[0], [o.strip() for o in parts[1].split(",")] if len(parts) > 1 else []
 
 
-# kernels whose direct loads are hand-written: mask kind 0 (none) of the
-# bf16 and fp32 kernels, and the streaming kernel
-HAND = re.compile(r"fwd_(bf16|f32)_kernelILi\d+ELi0E|fwd_bf16_stream_kernel")
+# kernels whose direct loads are hand-written: every bf16 work-group kernel,
+# mask kind 0 (none) of the fp32 kernels, and the streaming kernel
+HAND = re.compile(r"fwd_bf16_kernelILi\d+ELi\d+E|fwd_f32_kernelILi\d+ELi0E|fwd_bf16_stream_kernel")
 
 
 def test_m0_is_set_right_before_each_reader(tmp_path):
