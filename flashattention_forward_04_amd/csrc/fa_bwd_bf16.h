@@ -40,6 +40,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace fa {
 namespace {
 
@@ -300,8 +302,10 @@ bwd_dq_kernel(const BwdParams p)
 }
 
 // ---------------------------------------------------------------- dK, dV
-// KVS: the grid is split over each group's heads (fp32 partials); the
-// unsplit kernel is a separate instantiation so that its code is unchanged.
+// KVS: the grid is split kv_split ways per key tile (fp32 partials): the
+// work-group of split s takes steps s, s + kv_split, ... of the key tile's
+// (query head, query tile) steps.  The unsplit kernel is a separate
+// instantiation so that its code is unchanged.
 template <int D, int MASK, bool CAUSAL, int NW, int BQ, int WPE, bool KVS>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 bwd_dkdv_kernel(const BwdParams p)
@@ -324,16 +328,13 @@ bwd_dkdv_kernel(const BwdParams p)
 
     // kv head innermost: with H_kv a multiple of 8 every work-group of a kv
     // head runs on one XCD and re-reads that group's Q and dO from its L2.
-    // A split grid gives each of kv_split work-groups of a key tile
-    // group / kv_split consecutive query heads of the group.
     int id = blockIdx.x;
     const int hk = id % p.Hkv;
     id /= p.Hkv;
     const int kvs = KVS ? p.kv_split : 1;
-    const int split = id % kvs;
+    const int split = KVS ? id % kvs : 0;
     id /= kvs;
-    const int gps = p.group / kvs;  // query heads per work-group
-    const int h_first = hk * p.group + split * gps;
+    const int h_first = hk * p.group;
     const int b = id % p.B;
     id /= p.B;
     const int k0 = id * BK;  // causal: the first key tiles see the most queries (issued first)
@@ -366,11 +367,15 @@ bwd_dkdv_kernel(const BwdParams p)
     const int qt0 = CAUSAL ? min(k0, p.qL) / BQ : 0;
     const int n_qt = (p.qL + BQ - 1) / BQ;
     const int per_head = max(0, n_qt - qt0);
-    const int n_steps = (k0 < p.kL) ? per_head * gps : 0;
+    // the key tile's steps (query head, query tile); a split work-group takes
+    // every kvs-th of them, from its own
+    const int n_all = (k0 < p.kL) ? per_head * p.group : 0;
+    const int n_steps = KVS ? (n_all > split ? (n_all - split + kvs - 1) / kvs : 0) : n_all;
+    auto at = [&](int step) __attribute__((always_inline)) { return KVS ? split + step * kvs : step; };
 
     auto stage = [&](int step, int buf) __attribute__((always_inline)) {
-        const int h = h_first + step / per_head;
-        const int q0 = (qt0 + step % per_head) * BQ;
+        const int h = h_first + at(step) / per_head;
+        const int q0 = (qt0 + at(step) % per_head) * BQ;
         const int64_t qoff = (((int64_t)b * p.Hq + h) * p.qL) * D;
         bwd_stage_rows<D, TP, BQ, NW>((const uint16_t*)p.q + qoff, D, q0, p.qL, Qs[buf], wave, lane);
         bwd_stage_rows<D, TP, BQ, NW>((const uint16_t*)p.dout + qoff, D, q0, p.qL, Os[buf], wave, lane);
@@ -389,8 +394,8 @@ bwd_dkdv_kernel(const BwdParams p)
         bwd_wait_loads();
         __syncthreads();  // this step's tiles are in LDS; buffer buf ^ 1 is free
         if (step + 1 < n_steps) stage(step + 1, buf ^ 1);
-        const int h = h_first + step / per_head;
-        const int q0 = (qt0 + step % per_head) * BQ;
+        const int h = h_first + at(step) / per_head;
+        const int q0 = (qt0 + at(step) % per_head) * BQ;
         // a wave whose keys all follow the tile's last row skips it
         if (wk0 >= p.kL) continue;
         if (CAUSAL && wk0 > q0 + BQ - 1) continue;
@@ -554,17 +559,23 @@ __global__ void __launch_bounds__(256) bwd_dkdv_reduce_kernel(const BwdParams p)
     *(bwd_u32x2*)((uint16_t*)p.dv + e) = wv;
 }
 
-// Heads of a GQA group per dK/dV work-group: a grid with fewer work-groups
-// than CUs splits each group's query heads over up to 512 / work-groups of
-// them (a divisor of the group size).
-inline int bwd_kv_split(int64_t kv_wgs, int group)
+// Work-groups each key tile's steps are split over (1: none).  A grid with
+// fewer work-groups than CUs splits them over up to 512 / work-groups.  A
+// causal grid of up to ~two resident rounds splits them too: its first key
+// tiles see every query tile and its last almost none, and with every
+// work-group resident at once the launch lasts as long as the longest one
+// (at 32 heads x 8192 keys, 1024 steps against 520 on average); split, the
+// longest takes half as many steps and the rest fill in behind it.  Up to
+// 1024 work-groups then, and at most kMaxSplit ways.
+#ifndef FA_BWD_CAUSAL_MAX_WGS
+#define FA_BWD_CAUSAL_MAX_WGS 1024
+#endif
+inline int bwd_kv_split(int64_t kv_wgs, bool causal)
 {
-    constexpr int kCUs = 256, kMaxWgs = 512;
-    if (kv_wgs <= 0 || kv_wgs >= kCUs) return 1;
-    int ns = 1;
-    for (int d = 2; d <= group; ++d)
-        if (group % d == 0 && kv_wgs * d <= kMaxWgs) ns = d;
-    return ns;
+    constexpr int kCUs = 256, kMaxWgs = 512, kMaxSplit = 16;
+    if (kv_wgs <= 0 || (kv_wgs >= kCUs && !causal)) return 1;
+    const int64_t cap = (kv_wgs >= kCUs) ? FA_BWD_CAUSAL_MAX_WGS : kMaxWgs;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(kMaxSplit, cap / kv_wgs));
 }
 
 // Launch shapes: work-group waves and tile rows of the dQ and dK/dV grids.
@@ -582,7 +593,7 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t st)
     if (err != hipSuccess) return err;
     const int64_t kv_wgs = (int64_t)((p.kL + KNW * 32 - 1) / (KNW * 32)) * p.Hkv * p.B;
     BwdParams q = p;
-    q.kv_split = bwd_kv_split(kv_wgs, p.group);
+    q.kv_split = bwd_kv_split(kv_wgs, CAUSAL);
     q.kv_part = nullptr;
     if (q.kv_split == 1) {
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK, CAUSAL, KNW, BQ, KWPE, false>), dim3((unsigned)kv_wgs),

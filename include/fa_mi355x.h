@@ -224,12 +224,14 @@ fa_status fa_fwd_window(const void* Q, const void* K, const void* V, const void*
  * FA_ERR_UNSUPPORTED.  Three launches on `hip_stream` (Delta, then dQ, then
  * dK and dV); no atomics, so the result is deterministic.  When the dK/dV
  * grid would leave CUs idle (fewer than 256 work-groups of 128 keys, e.g.
- * B = 2, H_kv = 4, kL = 2048) and H_q / H_kv > 1, each GQA group's query
- * heads are split over up to 512 / work-groups of them; their fp32 partial
- * dK and dV (2 * split * B * H_kv * kL * D * 4 bytes, at most ~67 MB) come
- * from the library's stream-ordered pool (as fa_fwd's split partials) and
- * are summed, in a fixed order, by a fourth launch.  Otherwise nothing is
- * allocated.  Checks as fa_fwd, plus dO, Delta, dQ, dK, dV non-NULL and
+ * B = 2, H_kv = 4, kL = 2048), or is causal with at most 1023 work-groups
+ * (its first key tiles see every query tile, e.g. B = 1, H_kv = 8,
+ * kL = 8192), each key tile's (query head, query tile) steps are split over
+ * up to 16 work-groups (at most 512 in all, 1024 if causal); their fp32
+ * partial dK and dV (2 * split * B * H_kv * kL * D * 4 bytes, at most
+ * ~134 MB) come from the library's stream-ordered pool (as fa_fwd's split
+ * partials) and are summed, in a fixed order, by a fourth launch.
+ * Otherwise nothing is allocated.  Checks as fa_fwd, plus dO, Delta, dQ, dK, dV non-NULL and
  * aligned (16 bytes; 4 for L and Delta).
  */
 fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* L,

@@ -113,8 +113,9 @@ def test_shapes(D, causal, qL, kL):
 @pytest.mark.parametrize("Hq,Hkv,kind,causal", [(16, 2, "none", False), (16, 2, "bool", True), (24, 4, "additive", False),
                                                (8, 8, "none", True)], ids=lambda x: str(x))
 def test_group_splits(D, Hq, Hkv, kind, causal):
-    """Small dK/dV grids split over each group's heads in 8 (group 8), 6
-    (group 6) and 1 (MHA) ways; the partials are summed in a fixed order."""
+    """Small dK/dV grids whose key tiles' (head, query tile) steps are split
+    over up to 16 work-groups (GQA groups of 8 and 6, and MHA); the partials
+    are summed in a fixed order."""
     _case(1, Hq, Hkv, 200, 333, D, causal, 650 + D + Hq, mask_kind=kind, empty_row=kind != "none")
 
 
