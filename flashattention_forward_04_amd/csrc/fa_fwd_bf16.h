@@ -1332,7 +1332,16 @@ fwd_bf16_split_kernel(const FwdParams p)
 //     query-head group; the next block's Q is loaded into registers while
 //     the current block is computed and its O stored (the raw words are
 //     converted only where they are used, so nothing waits for them early);
-//   * the grid is sized to the number of work-groups the GPU holds at once.
+//   * the grid is sized to the number of work-groups the GPU holds at once;
+//   * O leaves through a small per-wave LDS region, so that each store
+//     covers whole 128-byte lines of 8 rows (stored straight from the
+//     accumulators, an instruction writes 16 bytes of each of 32 rows, and
+//     those scattered writes cost more than the rest of the kernel: 40
+//     against 30 us at 32 heads x 8192 rows x 32 keys, 26.5 with the whole
+//     lines stored nontemporally; a nontemporal hint on the scattered pieces
+//     made it 4x slower).  With NT = 4 and 4 waves there is no LDS room for
+//     the region beside two work-groups per CU, so NT = 4 takes 8-wave
+//     work-groups, one per CU.
 template <int D, bool CAUSAL, int NW, int NT>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_stream_kernel(const FwdParams p, int wgs_per_head)
@@ -1346,6 +1355,11 @@ fwd_bf16_stream_kernel(const FwdParams p, int wgs_per_head)
     constexpr int DK = D / 16, ND = D / 32;
     __shared__ __attribute__((aligned(1024))) uint16_t Ks[NT * KTILE];
     __shared__ __attribute__((aligned(1024))) uint16_t Vs[NT * VTILE];
+    // O staging: per wave 32 rows x 64 columns (128 bytes of a row), pitch
+    // 72 elements
+    constexpr bool STAGE = (NT <= 2 || NW == 8) && D % 64 == 0;
+    constexpr int OP = 72;
+    __shared__ __attribute__((aligned(16))) uint16_t Ost[STAGE ? NW * 32 * OP : 8];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1476,18 +1490,50 @@ fwd_bf16_stream_kernel(const FwdParams p, int wgs_per_head)
             }
             l_run += row_sum_halves(rs0 + rs1);
         }
-        if (qrow < p.qL) {
-            const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
-            uint16_t* orow = (uint16_t*)p.o + b * p.o_s[0] + h * p.o_s[1] + (int64_t)qrow * p.o_s[2];
+        const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
+        if constexpr (STAGE) {
+            // 64 columns at a time: the lanes' 4-element runs into the
+            // wave's region, then rows back out as 16-byte pieces, 8 lanes
+            // per row (the region is the wave's own, and a wave's LDS
+            // accesses take effect in order, so no barrier is needed)
+            uint16_t* xs = Ost + wave * (32 * OP);
+            uint16_t* obase = (uint16_t*)p.o + b * p.o_s[0] + h * p.o_s[1];
 #pragma unroll
-            for (int d = 0; d < ND; ++d)
+            for (int hc = 0; hc < D / 64; ++hc) {
 #pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    u32x2 w;
-                    w[0] = pack_bf16x2(o[d][4 * rq + 0] * inv, o[d][4 * rq + 1] * inv);
-                    w[1] = pack_bf16x2(o[d][4 * rq + 2] * inv, o[d][4 * rq + 3] * inv);
-                    *(u32x2*)(orow + 32 * d + 8 * rq + 4 * g) = w;
+                for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+                    for (int rq = 0; rq < 4; ++rq) {
+                        const int d = 2 * hc + dd;
+                        u32x2 w;
+                        w[0] = pack_bf16x2(o[d][4 * rq + 0] * inv, o[d][4 * rq + 1] * inv);
+                        w[1] = pack_bf16x2(o[d][4 * rq + 2] * inv, o[d][4 * rq + 3] * inv);
+                        *(u32x2*)(xs + r32 * OP + 32 * dd + 8 * rq + 4 * g) = w;
+                    }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rr = 8 * i + (lane >> 3), c8 = 8 * (lane & 7);
+                    const u32x4 v = *(const u32x4*)(xs + rr * OP + c8);
+                    // (nontemporal: O is not read again here; whole lines
+                    // so marked go out without a read-modify-write)
+                    if (q0 + rr < p.qL)
+                        __builtin_nontemporal_store(v, (u32x4*)(obase + (int64_t)(q0 + rr) * p.o_s[2] + 64 * hc + c8));
                 }
+            }
+        }
+        if (qrow < p.qL) {
+            if constexpr (!STAGE) {
+                uint16_t* orow = (uint16_t*)p.o + b * p.o_s[0] + h * p.o_s[1] + (int64_t)qrow * p.o_s[2];
+#pragma unroll
+                for (int d = 0; d < ND; ++d)
+#pragma unroll
+                    for (int rq = 0; rq < 4; ++rq) {
+                        u32x2 w;
+                        w[0] = pack_bf16x2(o[d][4 * rq + 0] * inv, o[d][4 * rq + 1] * inv);
+                        w[1] = pack_bf16x2(o[d][4 * rq + 2] * inv, o[d][4 * rq + 3] * inv);
+                        *(u32x2*)(orow + 32 * d + 8 * rq + 4 * g) = w;
+                    }
+            }
             if (g == 0) {
                 const float lse = (l_run > 0.f) ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : 0.f;
                 p.lse[((int64_t)b * p.Hq + h) * p.qL + qrow] = lse;
@@ -1549,7 +1595,18 @@ hipError_t launch_bf16_any(const FwdParams& p, hipStream_t st, size_t* need = nu
                 *need = 0;
                 return hipSuccess;
             }
-            hipLaunchKernelGGL((fwd_bf16_stream_kernel<D, CAUSAL, 4, 4>), grid, dim3(4 * 64), 0, st, p, per_head);
+            // K/V LDS sized to the key range (one, two or four 32-key tiles)
+            if (p.kL <= 32)
+                hipLaunchKernelGGL((fwd_bf16_stream_kernel<D, CAUSAL, 4, 1>), grid, dim3(4 * 64), 0, st, p, per_head);
+            else if (p.kL <= 64)
+                hipLaunchKernelGGL((fwd_bf16_stream_kernel<D, CAUSAL, 4, 2>), grid, dim3(4 * 64), 0, st, p, per_head);
+            else {
+                // 8-wave work-groups, one per CU
+                int per_head8 = (kResident / 2 + heads - 1) / heads;
+                per_head8 = max(1, min(per_head8, blocks / 8));
+                hipLaunchKernelGGL((fwd_bf16_stream_kernel<D, CAUSAL, 8, 4>), dim3((unsigned)(per_head8 * heads)),
+                                   dim3(8 * 64), 0, st, p, per_head8);
+            }
             return hipGetLastError();
         }
     }
