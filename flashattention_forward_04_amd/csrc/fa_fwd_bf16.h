@@ -837,6 +837,58 @@ fwd_bf16_kernel(const FwdParams p)
     }
 
     // ---- epilogue: O = O / l, L = (m + log2 l) ln2 (O = 0, L = 0 if no key) ----
+    // Per-wave regions of the (by now idle) K/V buffers for whole-line
+    // stores: 32 rows of XP floats, or of 2 XP bf16 elements.
+    constexpr int XP = 36;                        // region row pitch, floats
+    constexpr int XE = 32 * XP * 2;               // region size in 16-bit elements
+    constexpr int RK = KTILE / XE, RV = VTILE / XE;
+    constexpr bool XPOSE = 2 * RK + 2 * RV >= NW;  // (every wave gets a region)
+    auto region = [&](int w) __attribute__((always_inline)) -> uint16_t* {
+        return w < RK ? Ks0 + w * XE : w < 2 * RK ? Ks1 + (w - RK) * XE
+                    : w < 2 * RK + RV ? Vs0 + (w - 2 * RK) * XE : Vs1 + (w - 2 * RK - RV) * XE;
+    };
+    if constexpr (XPOSE && D % 64 == 0 && !RPACK) {
+        if (p.n_split == 1 && p.head_pack == 0) {
+            // O of an unsplit launch: stored straight from the accumulators,
+            // an instruction writes 16 bytes of each of 32 rows; instead each
+            // wave passes 64 columns at a time through its region and stores
+            // whole 128-byte lines of 8 rows, nontemporally (O is not read
+            // again here)
+            __syncthreads();  // every wave (both key halves) is past its last read of the K/V buffers
+            if (KSPLIT && half != 0) return;  // half 0 writes the merged rows
+            const float inv = (l_run > 0.f) ? (DROP ? p.drop_scale : 1.f) / l_run : 0.f;
+            constexpr int OP = 2 * XP;  // region row pitch, bf16 elements
+            uint16_t* xs = region(wave);
+            uint16_t* obase = (uint16_t*)p.o + b * p.o_s[0] + h * p.o_s[1];
+#pragma unroll
+            for (int hc = 0; hc < D / 64; ++hc) {
+#pragma unroll
+                for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+                    for (int rq = 0; rq < 4; ++rq) {
+                        const int d = 2 * hc + dd;
+                        u32x2 w;
+                        w[0] = pack_bf16x2(o[d][4 * rq + 0] * inv, o[d][4 * rq + 1] * inv);
+                        w[1] = pack_bf16x2(o[d][4 * rq + 2] * inv, o[d][4 * rq + 3] * inv);
+                        *(u32x2*)(xs + r32 * OP + 32 * dd + 8 * rq + 4 * g) = w;
+                    }
+                // (the region is this wave's own, and a wave's LDS accesses
+                // take effect in order)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rr = 8 * i + (lane >> 3), c8 = 8 * (lane & 7);
+                    const u32x4 v = *(const u32x4*)(xs + rr * OP + c8);
+                    if (wq0 + rr < p.qL)
+                        __builtin_nontemporal_store(v, (u32x4*)(obase + (int64_t)(wq0 + rr) * p.o_s[2] + 64 * hc + c8));
+                }
+            }
+            if (qrow < p.qL && g == 0) {
+                const float lse = (l_run > 0.f) ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : 0.f;
+                p.lse[((int64_t)b * p.Hq + h) * p.qL + qrow] = lse;
+            }
+            return;
+        }
+    }
     if (KSPLIT && half != 0) return;  // half 0 writes the merged rows
     if (p.n_split > 1) {
         // one key range of a split launch: normalised fp32 O and natural-log
@@ -852,17 +904,9 @@ fwd_bf16_kernel(const FwdParams p)
         // 32 x XP float region of the (by now idle) K/V buffers, one 32-column
         // block at a time, and each store then covers whole 128-byte lines
         // of four rows.
-        constexpr int XP = 36;                        // region row pitch, floats
-        constexpr int XE = 32 * XP * 2;               // region size in 16-bit elements
-        constexpr int RK = KTILE / XE, RV = VTILE / XE;
-        constexpr bool XPOSE = 2 * RK + 2 * RV >= NW;  // (every wave gets a region)
         if constexpr (XPOSE) {
             __syncthreads();  // every wave is past its last read of the K/V buffers
-            const int w = wave;
-            float* xs = (float*)(w < RK             ? Ks0 + w * XE
-                                 : w < 2 * RK       ? Ks1 + (w - RK) * XE
-                                 : w < 2 * RK + RV  ? Vs0 + (w - 2 * RK) * XE
-                                                    : Vs1 + (w - 2 * RK - RV) * XE);
+            float* xs = (float*)region(wave);
             // this wave's first row (RPACK: of the wave's first head; its
             // second head's rows start 16 region rows later)
             const int64_t row0 = ((int64_t)b * p.Hq + (RPACK ? hk * p.group + (h - hk * p.group) / 2 * 2 : h)) * p.qL + wq0;
