@@ -100,6 +100,12 @@ __device__ __forceinline__ void bwd_stage_rows(const uint16_t* gbase, int64_t st
 template <int ROWS, int PITCH>
 constexpr int bwd_tile_elems() { return ((ROWS * PITCH / 8 + 63) / 64) * 512; }
 
+// Row pitch padding (elements) of the tiles read both as rows and by
+// transposing reads (K in the dQ grid, Q and dO in the dK/dV grid).
+#ifndef FA_BWD_TILE_PAD
+#define FA_BWD_TILE_PAD 24
+#endif
+
 __device__ __forceinline__ void bwd_wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // ---------------------------------------------------------------- Delta
@@ -134,7 +140,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 bwd_dq_kernel(const BwdParams p)
 {
     constexpr int BM = NW * 32;
-    constexpr int KP = D + 32;  // K tile pitch: row reads and transposing reads
+    constexpr int KP = D + FA_BWD_TILE_PAD;  // K tile pitch: row reads and transposing reads
     constexpr int VP = D + 8;   // V tile pitch: row reads only
     constexpr int KT = bwd_tile_elems<BN, KP>();
     constexpr int VT = bwd_tile_elems<BN, VP>();
@@ -311,7 +317,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 bwd_dkdv_kernel(const BwdParams p)
 {
     constexpr int BK = NW * 32;  // keys per work-group
-    constexpr int TP = D + 32;   // Q and dO tile pitch: row reads and transposing reads
+    constexpr int TP = D + FA_BWD_TILE_PAD;  // Q and dO tile pitch: row reads and transposing reads
     constexpr int TT = bwd_tile_elems<BQ, TP>();
     constexpr int DK = D / 16;
     constexpr int NQ = BQ / 32;  // 32-query blocks per tile
