@@ -127,11 +127,33 @@ constexpr float kRescaleSlack = 8.f;
 #endif
 
 // K and V tiles live in LDS row-major ([BN][D], one key per row) with a
-// padded row pitch: D + 8 elements for K, D + 32 for V.  Measured on gfx950
-// (for D = 64, 128 and 256) these pitches have no bank conflicts for the
-// 16-byte staging writes, the 16-byte K operand reads and the transposing V
-// operand reads, and they keep every operand address a per-lane base plus a
+// padded row pitch: D + 8 elements for K; for V, D + 32, or 96 at D = 48
+// and 80.  Measured on gfx950, the K pitch has no bank conflicts for the
+// 16-byte staging writes and the 16-byte K operand reads, and the
+// transposing V reads are conflict-free when the V pitch is 32 elements
+// past a multiple of 64 (D + 32 is that at D = 64, 128 and 256).  At
+// D = 16, 32 and 96 such a pitch removed the conflicts (up to 33 % of CU
+// cycles at D = 96) without making the kernel faster, so those keep D + 32.
+// The pitches keep every operand address a per-lane base plus a
 // compile-time offset.
+template <int D>
+constexpr int k_pitch()
+{
+#ifdef FA_BF16_KPAD
+    return D + FA_BF16_KPAD;
+#else
+    return D + 8;
+#endif
+}
+template <int D>
+constexpr int v_pitch()
+{
+#ifdef FA_BF16_VPAD
+    return D + FA_BF16_VPAD;
+#else
+    return (D == 48 || D == 80) ? 96 : D + 32;
+#endif
+}
 template <int P>
 struct TileLayout {
     static constexpr int PITCH = P;
@@ -183,8 +205,8 @@ fwd_bf16_kernel(const FwdParams p)
     constexpr int NH = KSPLIT ? 2 : 1;  // key halves
     constexpr int WH = NW / NH;         // waves per half; the halves share the query rows
     constexpr int BM = WH * 32;         // query rows per work-group
-    using KL = TileLayout<D + 8>;     // K tile layout in LDS
-    using VL = TileLayout<D + 32>;    // V tile layout in LDS
+    using KL = TileLayout<k_pitch<D>()>;  // K tile layout in LDS
+    using VL = TileLayout<v_pitch<D>()>;  // V tile layout in LDS
     // tiles are padded to whole 1 KiB blocks: one direct load of a wave
     // fills exactly one block
     constexpr int KSPR = KL::PITCH / 8;          // 16-byte slots per K row
@@ -201,7 +223,8 @@ fwd_bf16_kernel(const FwdParams p)
     constexpr int ND = (D + 31) / 32;
     constexpr int NP = DK * NC;                  // score products per tile
     static_assert(BN % 32 == 0 && D % 16 == 0, "tile shape");
-    static_assert(32 * ND <= D + 32, "the V^T reads of the last block stay inside a padded V row");
+    static_assert(32 * ND <= v_pitch<D>(), "the V^T reads of the last block stay inside a padded V row");
+    static_assert(k_pitch<D>() % 8 == 0 && v_pitch<D>() % 8 == 0, "16-byte rows");
 
     // NB buffers each for K and V, as separate arrays so that the compiler
     // can tell the buffer being loaded from the ones being read
@@ -968,7 +991,7 @@ fwd_bf16_kernel(const FwdParams p)
 template <int D, int NW, int BN, int WPE, int NB>
 constexpr int wgs_per_cu()
 {
-    constexpr int kLdsPerWg = NB * ((BN * (D + 8) / 8 + 63) / 64 + (BN * (D + 32) / 8 + 63) / 64) * 1024;
+    constexpr int kLdsPerWg = NB * ((BN * k_pitch<D>() / 8 + 63) / 64 + (BN * v_pitch<D>() / 8 + 63) / 64) * 1024;
     return (4 * WPE / NW < 160 * 1024 / kLdsPerWg) ? 4 * WPE / NW : 160 * 1024 / kLdsPerWg;
 }
 
@@ -1072,8 +1095,8 @@ template <int D, int MASK, bool CAUSAL, int NS, int BN>
 __global__ void __launch_bounds__(NS * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 fwd_bf16_split_kernel(const FwdParams p)
 {
-    using KL = TileLayout<D + 8>;
-    using VL = TileLayout<D + 32>;
+    using KL = TileLayout<k_pitch<D>()>;
+    using VL = TileLayout<v_pitch<D>()>;
     constexpr int KSPR = KL::PITCH / 8;
     constexpr int VSPR = VL::PITCH / 8;
     constexpr int KINS = (BN * KSPR + 63) / 64;  // 1 KiB blocks (and loads) per K tile
@@ -1391,8 +1414,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
 fwd_bf16_stream_kernel(const FwdParams p, int wgs_per_head)
 {
     constexpr int BN = 32;
-    using KL = TileLayout<D + 8>;
-    using VL = TileLayout<D + 32>;
+    using KL = TileLayout<k_pitch<D>()>;
+    using VL = TileLayout<v_pitch<D>()>;
     constexpr int KSPR = KL::PITCH / 8, VSPR = VL::PITCH / 8;
     constexpr int KINS = (BN * KSPR + 63) / 64, VINS = (BN * VSPR + 63) / 64;
     constexpr int KTILE = KINS * 512, VTILE = VINS * 512;
