@@ -278,6 +278,46 @@ def test_token_major_equals_head_major():
     assert raw.stride() == (77 * 3 * 128, 128, 3 * 128, 1)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,qL,kL,D,causal,kind", [
+    (1, 4, 2, 1000, 700, 128, False, "none"),    # 8-wave work-groups, ragged last query tile
+    (1, 4, 2, 333, 1111, 128, True, "bool"),
+    (2, 16, 4, 600, 600, 64, True, "none"),      # grid resident at once: causal key halves
+    (1, 6, 3, 777, 300, 64, False, "additive"),
+    (1, 16, 4, 2000, 300, 256, False, "none"),   # D = 256 work-group kernel (256 query tiles)
+    (1, 16, 8, 2047, 129, 256, True, "additive"),
+], ids=lambda x: str(x))
+def test_whole_line_output_stores(B, Hq, Hkv, qL, kL, D, causal, kind):
+    """The unsplit epilogue passes O through LDS and stores whole lines of 8
+    rows: token-major and head-major O, ragged query ranges (rows past qL
+    are not written: the buffer's guard rows keep their sentinel), against
+    the oracle and each other."""
+    print(f"[case] whole-line O B={B} Hq={Hq} Hkv={Hkv} qL={qL} kL={kL} D={D} causal={causal} mask={kind}",
+          flush=True)
+    q, k, v = _rand((B, Hq, qL, D), BF16, 95), _rand((B, Hkv, kL, D), BF16, 96), _rand((B, Hkv, kL, D), BF16, 97)
+    mask = None
+    if kind != "none":
+        rng = np.random.default_rng(98)
+        masked = W.draw_masked(rng, (B, Hq, qL, kL), 0.3)
+        if kind == "bool":
+            mask = torch.from_numpy((~masked).astype(np.uint8))
+        else:
+            m = rng.standard_normal(masked.shape).astype(np.float32)
+            m[masked] = -np.inf
+            mask = torch.from_numpy(m).to(BF16)
+    scale = 1 / math.sqrt(D)
+    dev = torch.device("cuda:0")
+    # token-major O inside a buffer with one guard row on each side
+    buf = torch.full((B, qL + 2, Hq, D), 7.0, dtype=BF16, device=dev)
+    out = buf[:, 1:qL + 1].transpose(1, 2)
+    O1, L1, _ = run_gpu(q, k, v, mask, causal=causal, scale=scale, out=out)
+    O2, L2, _ = run_gpu(q, k, v, mask, causal=causal, scale=scale)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    g = buf.float().cpu()
+    assert torch.all(g[:, 0] == 7.0) and torch.all(g[:, qL + 1] == 7.0)
+    Oref, Lref = run_oracle(q, k, v, mask, causal=causal, scale=scale)
+    assert_parity(O2, L2, Oref, Lref, "bf16", f"whole-line O qL={qL} kL={kL} D={D}")
+
+
 def test_negative_and_zero_scale():
     q, k, v = _rand((1, 2, 64, 64), BF16, 32), _rand((1, 2, 80, 64), BF16, 33), _rand((1, 2, 80, 64), BF16, 34)
     for scale in (-0.2, 0.0):
