@@ -531,8 +531,11 @@ def main():
         fa.fwd(qd, kd, vd, mask=md, causal=w.causal, scale=w.scale, out=out, lse=lse, stream=stream,
                dropout_p=w.dropout_p, seed=w.seed, window=w.window)
 
-    # per-launch kernel durations from HIP events on the launch stream, for
-    # the warm-up launches too (they show how the clock settles)
+    # HIP events on the launch stream: around each warm-up call (they show
+    # how the clock settles), and one pair around the timed region, whose
+    # calls run back to back.  (An event pair per timed call costs the host
+    # ~9 us per call; calls of a few tens of us would then be timed at the
+    # host's pace, with the GPU idle between them.)
     def events(n):
         return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
@@ -541,27 +544,25 @@ def main():
         a.record(stream)
         step(i)
         b.record(stream)
-    evs = events(args.steps)
+    ta, tb = events(1)[0]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
+    ta.record(stream)
+    for i in range(args.steps):
         step(args.warmup + i)
-        b.record(stream)
+    tb.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
     warm_ms = [a.elapsed_time(b) for a, b in wev]
     log("per-launch us, warm-up: " + " ".join(f"{x * 1e3:.0f}" for x in warm_ms))
-    log("per-launch us, timed:   " + " ".join(f"{x * 1e3:.0f}" for x in kern_ms))
-    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    kern_avg_ms = ta.elapsed_time(tb) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
     flops = w.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kern_avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    log(f"kernel avg {kern_avg_ms * 1e3:.1f} us (min {min(kern_ms) * 1e3:.1f}, max {max(kern_ms) * 1e3:.1f}); "
+    log(f"kernel avg {kern_avg_ms * 1e3:.1f} us over the {args.steps} timed calls; "
         f"{achieved:.1f} TFLOP/s = {100 * achieved / peak:.1f}% of {peak} TFLOP/s")
     nbytes = algorithmic_bytes(w)
     log(f"algorithmic bytes {nbytes / 1e6:.1f} MB -> {nbytes / (kern_avg_ms * 1e-3) / 1e9:.0f} GB/s "

@@ -29,14 +29,20 @@
  *   - Allocation: the forward path allocates no device memory, with one
  *     stated exception.  A call (bf16 or fp32) whose grid of query tiles
  *     leaves most CUs idle while its key range is long splits that range
- *     over work-groups, and takes fp32 partials (n_split * B * H_q * qL *
- *     (D + 1) * 4 bytes) from a stream-ordered memory pool that the library
- *     creates for itself on each device (hipMemPoolCreate; it keeps up to
- *     256 MiB of freed memory for reuse).  They are returned to that pool on
- *     `hip_stream` after the merge.  The device's default pool and every
- *     other process-wide allocator setting are left untouched.  Callers that
- *     cannot allocate use fa_fwd_strided_noalloc.  fa_bwd takes the partials
- *     of a split dK/dV grid from the same pool (see fa_bwd).
+ *     over work-groups, and needs fp32 partials (n_split * B * H_q * qL *
+ *     (D + 1) * 4 bytes, at most ~34 MB).  They go to a workspace the
+ *     library keeps for each (device, stream) pair it has been called with,
+ *     taken from a stream-ordered memory pool that the library creates for
+ *     itself on each device (hipMemPoolCreate; it keeps up to 256 MiB of
+ *     freed memory for reuse) and grown, on `hip_stream`, when a call needs
+ *     more than it holds.  Each use waits for the previous one through an
+ *     event.  A workspace is held until the process ends; a device keeps at
+ *     most 8, and calls on further streams take their partials from the pool
+ *     per call and return them after the merge.  The device's default pool
+ *     and every other process-wide allocator setting are left untouched.
+ *     Callers that cannot allocate use fa_fwd_strided_noalloc.  fa_bwd takes
+ *     the partials of a split dK/dV grid from the same pool, per call (see
+ *     fa_bwd).
  *   - All argument checks run before any launch: a failed check writes
  *     nothing, launches nothing and returns FA_ERR_INVALID_ARGUMENT (or
  *     FA_ERR_UNSUPPORTED for a valid combination that is not built), with a

@@ -758,6 +758,57 @@ def test_split_launch_leaves_the_default_pool_alone():
     assert _default_pool_release_threshold() == before
 
 
+def test_split_workspace_reuse_across_streams():
+    """Split launches keep their partials in a workspace per (device, stream)
+    that grows when a call needs more: calls of growing and shrinking size,
+    bf16 and fp32, enqueued on two streams without synchronising in between,
+    and calls on more streams than the library keeps workspaces for, match
+    the same calls run one by one (bit for bit) and the oracle."""
+    dev = torch.device("cuda:0")
+    shapes = [(32, 8, 16, 8192, 128, BF16), (32, 8, 16, 32768, 128, BF16), (8, 2, 5, 3000, 64, F32),
+              (16, 4, 16, 20000, 256, BF16), (32, 8, 1, 12000, 128, BF16), (8, 2, 16, 9000, 128, F32)]
+    cases = []
+    for i, (Hq, Hkv, qL, kL, D, dt) in enumerate(shapes):
+        q, k, v = _rand((1, Hq, qL, D), dt, 300 + i), _rand((1, Hkv, kL, D), dt, 310 + i), _rand((1, Hkv, kL, D), dt, 320 + i)
+        cases.append((q.to(dev), k.to(dev), v.to(dev), 1 / math.sqrt(D)))
+    # one by one on the current stream
+    ref = []
+    for qd, kd, vd, sc in cases:
+        O, L = fa.fwd(qd, kd, vd, scale=sc)
+        torch.cuda.synchronize()
+        ref.append((O.clone(), L.clone()))
+    # interleaved on two streams, twice over, no synchronisation in between
+    s1, s2 = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+    outs = []
+    for rep in range(2):
+        for i, (qd, kd, vd, sc) in enumerate(cases):
+            st = s1 if (i + rep) % 2 == 0 else s2
+            with torch.cuda.stream(st):
+                outs.append(fa.fwd(qd, kd, vd, scale=sc, stream=st))
+    torch.cuda.synchronize()
+    for j, (O, L) in enumerate(outs):
+        Or, Lr = ref[j % len(cases)]
+        assert torch.equal(O, Or) and torch.equal(L, Lr), f"call {j} differs from the same call run alone"
+    # more streams than the library keeps workspaces for: the rest take
+    # their partials from the pool per call
+    extra = [torch.cuda.Stream(device=dev) for _ in range(10)]
+    outs = []
+    for j, st in enumerate(extra):
+        qd, kd, vd, sc = cases[j % len(cases)]
+        with torch.cuda.stream(st):
+            outs.append(fa.fwd(qd, kd, vd, scale=sc, stream=st))
+    torch.cuda.synchronize()
+    for j, (O, L) in enumerate(outs):
+        Or, Lr = ref[j % len(cases)]
+        assert torch.equal(O, Or) and torch.equal(L, Lr), f"extra-stream call {j} differs"
+    # and the results themselves, against the oracle
+    for (qd, kd, vd, sc), (Or, Lr) in zip(cases, ref):
+        q, k, v = qd.cpu(), kd.cpu(), vd.cpu()
+        Oref, Lref = run_oracle(q, k, v, scale=sc)
+        assert_parity(Or.double().cpu().numpy(), Lr.double().cpu().numpy(), Oref, Lref, dtype_name(q),
+                      f"workspace case qL={q.shape[2]} kL={k.shape[2]} D={q.shape[3]}")
+
+
 @pytest.mark.parametrize("D", [16, 32, 48, 64])
 @pytest.mark.parametrize("kind", ["none", "additive", "bool"])
 @pytest.mark.parametrize("B,Hq,Hkv,qL,kL", [(1, 40, 8, 600, 600), (2, 24, 6, 700, 650), (1, 36, 4, 1100, 1025)],
