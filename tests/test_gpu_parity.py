@@ -187,6 +187,20 @@ def test_short_keys_streaming(qL, kL, causal):
     assert_parity(O, L, Oref, Lref, "bf16", f"streaming qL={qL} kL={kL} causal={causal}")
 
 
+@pytest.mark.parametrize("qL,causal", [(665, False), (1184, True)])
+def test_short_keys_streaming_many_blocks(qL, causal):
+    """The streaming kernel at 65-128 keys walks its query blocks round two
+    Q buffers.  With 256 kv heads each head gets one 8-wave work-group, so
+    wave w takes blocks w, w + 8, ...: qL = 665 (21 blocks) gives waves 3
+    and 2 blocks, qL = 1184 (37 blocks) 5 and 4, which leaves the loop at
+    each of its exits."""
+    H = 256
+    q, k, v = _rand((1, H, qL, 128), BF16, 51), _rand((1, H, 100, 128), BF16, 52), _rand((1, H, 100, 128), BF16, 53)
+    O, L, _ = run_gpu(q, k, v, None, causal=causal, scale=1 / math.sqrt(128))
+    Oref, Lref = run_oracle(q, k, v, None, causal=causal, scale=1 / math.sqrt(128))
+    assert_parity(O, L, Oref, Lref, "bf16", f"streaming many blocks qL={qL} causal={causal}")
+
+
 def test_bool_mask_equals_additive():
     q, k, v = _rand((1, 2, 64, 128), BF16, 8), _rand((1, 2, 96, 128), BF16, 9), _rand((1, 2, 96, 128), BF16, 10)
     attend = torch.from_numpy(np.random.default_rng(11).random((1, 2, 64, 96)) < 0.5)
