@@ -28,7 +28,8 @@
  *     stream) and returns without synchronising.
  *   - Allocation: the forward path allocates no device memory, with one
  *     stated exception.  A call (bf16 or fp32) whose grid of query tiles
- *     leaves most CUs idle while its key range is long splits that range
+ *     leaves most CUs idle while its key range is long (for fp32 grids of
+ *     at most 8 work-groups, two or more 32-key tiles) splits that range
  *     over work-groups, and needs fp32 partials (n_split * B * H_q * qL *
  *     (D + 1) * 4 bytes, at most ~34 MB).  They go to a workspace the
  *     library keeps for each (device, stream) pair it has been called with,
