@@ -266,6 +266,29 @@ def test_dominant_key_closed_form():
 
 
 @pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_row_max_growing_across_tiles(dtype, D, causal):
+    """Scores stepping up by 7 (natural units, ~10 in base 2) every 128 keys,
+    three times, so the running max is exceeded by more than the slack the
+    kernels allow before rescaling O and l, on several tiles of a row (128
+    keys span one or more tiles of every launch shape).  16 heads keep the
+    grids large enough that the key range is not split into single tiles.
+    The scores stay near 20, where fp32 still resolves them to ~1e-6."""
+    g = torch.Generator().manual_seed(31)
+    qL, kL = 160, 600
+    q = torch.randn((1, 16, qL, D), generator=g) * 0.3
+    k = torch.randn((1, 4, kL, D), generator=g) * 0.3
+    v = torch.randn((1, 4, kL, D), generator=g)
+    q[..., 0] = 1.0
+    k[..., 0] = torch.clamp(torch.arange(kL) // 128, max=3).to(torch.float32) * (7.0 / 0.125)
+    q, k, v = q.to(dtype), k.to(dtype), v.to(dtype)
+    O, L, _ = run_gpu(q, k, v, causal=causal, scale=0.125)
+    Oref, Lref = run_oracle(q, k, v, causal=causal, scale=0.125)
+    assert_parity(O, L, Oref, Lref, dtype_name(q), f"growing max D={D} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
 def test_causal_first_row(dtype):
     """Causal row 0 sees only key 0: O_0 = V_0 and L_0 = scale q_0.k_0."""
     q, k, v = _rand((2, 4, 130, 128), dtype, 23), _rand((2, 2, 130, 128), dtype, 24), _rand((2, 2, 130, 128), dtype, 25)
