@@ -362,7 +362,10 @@ fwd_f32_kernel(const FwdParams p)
     }
     auto load_v = [&](int t) __attribute__((always_inline)) {
         if ((t + 1) * BN <= p.kL && off32) {
-            const char* tbase = uniform_base(Vb + (int64_t)t * BN * p.v_s[2]);
+            // (formed from Vb itself, not through readfirstlane: the loads
+            // stay global ones; a pointer rebuilt from integers would make
+            // them flat loads, which an LDS-read wait also waits for)
+            const char* tbase = (const char*)(Vb + (int64_t)t * BN * p.v_s[2]);
 #pragma unroll
             for (int it = 0; it < VIT; ++it) {
                 const int u = tid + it * NT;
