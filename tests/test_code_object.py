@@ -106,3 +106,14 @@ def test_m0_is_set_right_before_each_reader(tmp_path):
                 problems.append(f"{name}: M0 read by {ins}")
     assert n_loads > 0, "no direct loads found: the scan is not seeing the kernels"
     assert not problems, "\n".join(problems[:20])
+
+
+def test_no_flat_memory_instructions(tmp_path):
+    """Every load and store in the library addresses global memory or LDS
+    explicitly.  A flat one (a pointer whose address space the compiler lost,
+    e.g. one rebuilt from integers) also counts against the LDS-read wait
+    counter, so an LDS wait placed for an operand read would wait for it too."""
+    kernels = _kernels(_disassemble(tmp_path))
+    assert kernels
+    problems = [f"{name}: {ins}" for name, body in kernels.items() for ins in body if ins.startswith("flat_")]
+    assert not problems, "\n".join(problems[:20])
