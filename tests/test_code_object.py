@@ -80,8 +80,9 @@ def _operands(ins):
 
 
 # kernels whose direct loads are hand-written: every bf16 work-group kernel,
-# mask kind 0 (none) of the fp32 kernels, and the streaming kernel
-HAND = re.compile(r"fwd_bf16_kernelILi\d+ELi\d+E|fwd_f32_kernelILi\d+ELi0E|fwd_bf16_stream_kernel")
+# mask kind 0 (none) of the fp32 kernels, the streaming kernel and the
+# backward dQ kernel
+HAND = re.compile(r"fwd_bf16_kernelILi\d+ELi\d+E|fwd_f32_kernelILi\d+ELi0E|fwd_bf16_stream_kernel|bwd_dq_kernel")
 
 
 def test_m0_is_set_right_before_each_reader(tmp_path):
