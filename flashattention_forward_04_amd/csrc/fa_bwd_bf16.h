@@ -581,9 +581,10 @@ __global__ void __launch_bounds__(256) bwd_dkdv_reduce_kernel(const BwdParams p)
     *(bwd_u32x2*)((uint16_t*)p.dv + e) = wv;
 }
 
-// Work-groups each key tile's steps are split over (1: none).  A grid with
-// fewer work-groups than CUs splits them over up to 512 / work-groups.  A
-// causal grid of up to ~two resident rounds splits them too: its first key
+// Work-groups each key tile's steps are split over (1: none).  A non-causal
+// grid with fewer work-groups than CUs splits them over up to 512 /
+// work-groups.  A causal grid (small, or of up to ~two resident rounds)
+// splits them over up to FA_BWD_CAUSAL_MAX_WGS / work-groups: its first key
 // tiles see every query tile and its last almost none, and with every
 // work-group resident at once the launch lasts as long as the longest one
 // (at 32 heads x 8192 keys, 1024 steps against 520 on average); split, the
@@ -596,7 +597,10 @@ inline int bwd_kv_split(int64_t kv_wgs, bool causal)
 {
     constexpr int kCUs = 256, kMaxWgs = 512, kMaxSplit = 16;
     if (kv_wgs <= 0 || (kv_wgs >= kCUs && !causal)) return 1;
-    const int64_t cap = (kv_wgs >= kCUs) ? FA_BWD_CAUSAL_MAX_WGS : kMaxWgs;
+    // (a small causal grid takes the causal cap too: at 2 x 4 kv heads x 2048
+    // keys, D = 64, 8 ways against 4 took the dK/dV kernel from 72 to 62 us
+    // and the reduction from 6.3 to 10.9, 5.5 us less per call)
+    const int64_t cap = causal ? FA_BWD_CAUSAL_MAX_WGS : kMaxWgs;
     return (int)std::max<int64_t>(1, std::min<int64_t>(kMaxSplit, cap / kv_wgs));
 }
 
